@@ -1,0 +1,226 @@
+/*
+ * specdec.h -- C ABI of the speculative-sampling hot path on MI355X (gfx950).
+ *
+ * The library computes one speculative round's GPU work: the target model's single
+ * verify pass over the K+1 drafted positions, the draft model's steps, and the
+ * modified rejection-sampling step (accept with min(1, p/q), resample the first
+ * rejection from norm(max(0, p - q)), bonus token when all K are accepted), plus the
+ * KV-cache append / roll-back that goes with them.
+ *
+ * Sources (web pages describing the method):
+ *   [ZSM]   "Accelerating Large Language Model Decoding with Speculative Sampling"
+ *           (zeroshotmind.com explainer of Chen et al.)
+ *   [CANON] "57 Speculative Decoding" (ml-canon)
+ *   [LENS]  "Speculative Decoding from Scratch -- How a Tiny Draft Model Speeds Up an
+ *           LLM Without Changing a Single Output" (ta-paperlens)
+ *   [GC]    "Speculative Decoding: Getting 3x Speedups Without Changing the Model"
+ *           (General Compute blog)
+ *   [NOTE]  "NOTE-159: Accelerating Large Language Model Decoding with Speculative
+ *           Sampling" (anthology-of-the-sota)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates and
+ *     frees every device buffer (weights, KV arena, lengths, logits, tokens, outputs,
+ *     workspace); no call allocates device memory, synchronises the device or throws.
+ *   - Compute calls are asynchronous on `stream` (a hipStream_t; 0 = null stream).
+ *     The caller keeps buffers alive until the stream work has finished.
+ *   - A handle (spec_model, spec_kv) is an opaque host object owned by the library;
+ *     use one handle from one stream at a time.
+ *   - Arguments the host can check are checked before anything is launched; a bad
+ *     call returns a negative spec_status and launches nothing.  Conditions only the
+ *     device can see (lengths, token ids, non-finite logits) are reported per row in
+ *     `row_status` bits (SPEC_ROW_*), and such a row is left well-defined.
+ *   - Indices are 0-based: drafts x~_0..x~_{K-1}; target logit rows P_0..P_K (row j
+ *     scores draft j, row K is the bonus row); draft rows Q_0..Q_{K-1}.
+ *   - Layouts are row-major, innermost index last.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_E_INVALID = -1,      /* null pointer, bad shape, bad knob value              */
+  SPEC_E_UNSUPPORTED = -2,  /* valid but not built: e.g. T = 0, V > 32768, no gfx950 */
+  SPEC_E_CAPACITY = -3,     /* workspace or arena smaller than the size query says  */
+  SPEC_E_HIP = -4           /* a HIP launch failed; see spec_last_hip_error()        */
+} spec_status;
+
+/* row_status bits (int32 per sequence row) */
+#define SPEC_ROW_NONFINITE 1        /* a logit row of this sequence held NaN/Inf: nothing emitted  */
+#define SPEC_ROW_Q_ZERO 2           /* q(x~_j) == 0 at an evaluated position (rule still total)   */
+#define SPEC_ROW_RESIDUAL_EMPTY 4   /* max(0, p - q) summed to 0 at the rejection: sampled P_a    */
+#define SPEC_ROW_KV_OVERFLOW 8      /* cache could not take the tokens: row skipped               */
+#define SPEC_ROW_BAD_TOKEN 16       /* token id outside [0, V): nothing emitted                   */
+
+enum { SPEC_FFN_GELU = 0, SPEC_FFN_SWIGLU = 1 };
+enum { SPEC_DT_F32 = 0, SPEC_DT_BF16 = 1 };
+
+/* Model shape (host).  Decoder-only, pre-norm, no biases, untied embedding and LM
+ * head, RMSNorm (eps), RoPE (theta, half-split pairs (i, i + hd/2)), causal MHA with
+ * 1/sqrt(hd) scaling.  GELU FFN: W1 [F,d], W2 [d,F]; SwiGLU: Wg, Wu [F,d], Wd [d,F].
+ * bf16 models: bf16 weights and activations into every matrix product, fp32
+ * accumulation, fp32 residual stream / norms / softmax / logits.  f32: all fp32. */
+typedef struct {
+  int n_layers, d_model, n_heads, head_dim, d_ffn, vocab;
+  int ffn_kind; /* SPEC_FFN_* */
+  int dtype;    /* SPEC_DT_*  */
+  float norm_eps, rope_theta;
+} spec_model_cfg;
+
+/* Sampling knobs applied to BOTH p and q before the rule ([NOTE] "Key results",
+ * robust-to-knobs item, and Recommendation R3), in the order temperature -> top-k ->
+ * top-p -> renormalise.  temperature > 0 (0 = greedy is not built: SPEC_E_UNSUPPORTED);
+ * top_k = 0 means off (0 <= top_k); top_p = 1 means off (0 < top_p <= 1).  Ties at a
+ * top-k or top-p threshold are all kept. */
+typedef struct {
+  float temperature;
+  int top_k;
+  float top_p;
+} spec_sampling;
+
+typedef struct spec_model spec_model; /* opaque */
+typedef struct spec_kv spec_kv;       /* opaque */
+
+/* ------------------------------------------------------------------ model --------- */
+
+/* Number of weight pointers spec_model_create expects for `cfg`. */
+int spec_model_n_weights(const spec_model_cfg* cfg);
+
+/* Bind a model to caller-owned device weights (the library keeps the pointers, copies
+ * nothing).  `weights` (host array of device pointers) in this order:
+ *   embed [V,d], head [V,d], norm_f [d] (fp32),
+ *   then per layer: norm1 [d] (fp32), wqkv [3d,d] (rows: q heads | k heads | v heads),
+ *   wo [d,d], norm2 [d] (fp32), then SwiGLU: wgate [F,d], wup [F,d], wdown [d,F]
+ *   or GELU: w1 [F,d], w2 [d,F].
+ * Matrices and embeddings are bf16 for SPEC_DT_BF16 and fp32 for SPEC_DT_F32.
+ * Returns SPEC_E_INVALID for a bad shape, count or null pointer; SPEC_E_UNSUPPORTED
+ * for a shape the kernels are not built for (bf16: head_dim 64 or 128 and d_model,
+ * d_ffn, vocab multiples of 16; f32: even head_dim <= 128) or a device that is not
+ * gfx950.  *out receives the handle. */
+spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
+                              int n_weights, spec_model** out);
+spec_status spec_model_destroy(spec_model* m);
+
+/* ------------------------------------------------------------------ KV cache ------ */
+
+/* Bytes of the KV arena for `batch` rows of up to `max_len` positions.  Layout:
+ * [n_layers][batch][2 (K,V)][n_heads][max_len][head_dim] elements (bf16 for bf16
+ * models, fp32 for f32), followed by 256-byte aligned per-row bookkeeping. */
+size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len);
+
+/* Bind a cache to a caller-owned arena of at least spec_kv_bytes() and to a caller-
+ * owned int32 length vector len[batch] (device; the number of valid positions of each
+ * row; the caller initialises it, usually to 0).  Nothing is launched. */
+spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, void* arena,
+                           size_t arena_bytes, int32_t* len, spec_kv** out);
+spec_status spec_kv_destroy(spec_kv* kv);
+
+/* Device pointer to the start of the arena's K/V element block (for seeding a cache
+ * with precomputed contents, e.g. a long prefilled context). */
+void* spec_kv_data(spec_kv* kv);
+
+/* Roll back: len[b] <- min(len[b], max(new_len[b], 0)).  Entries past the new length
+ * become stale and are overwritten by the next append.  [LENS] §2.1: drafts after the
+ * first rejection are discarded. */
+spec_status spec_kv_rollback(spec_kv* kv, const int32_t* new_len, void* stream);
+
+/* ------------------------------------------------------------------ forward ------- */
+
+/* Workspace bytes for spec_verify_forward / spec_draft_step with `batch` rows of up to
+ * `max_rows` new tokens each, over a cache of `max_len` positions. */
+size_t spec_workspace_bytes(const spec_model_cfg* cfg, int batch, int max_rows, int max_len);
+
+/* The verify pass ([ZSM] "One pass can score many tokens" and "The algorithm"; [LENS]
+ * §2.1 step 2; [GC] "How It Works" step 2): score n_tok[b] <= M new tokens per row at
+ * positions len[b] .. len[b]+n_tok[b]-1 in ONE pass over the weights and the cache,
+ * append their K/V and advance len[b] by n_tok[b].
+ *   tokens  [B, M] int32 (row b uses its first n_tok[b] entries)
+ *   n_tok   [B] int32 or NULL (= M for every row)
+ *   logits  [B, M, V] fp32 out (rows j >= n_tok[b] are written as 0)
+ *   row_status [B] int32 or NULL: OR-ed with SPEC_ROW_KV_OVERFLOW when
+ *           len[b] + n_tok[b] > max_len (the row is then not appended and its logits
+ *           are 0) and SPEC_ROW_BAD_TOKEN for a token id outside [0, V) (embedded as 0)
+ *   ws      workspace of ws_bytes >= spec_workspace_bytes(cfg, B, M, kv max_len)
+ * Used for the verify (n_tok = K+1), for draft steps (1 or 2) and for chunked prefill.
+ * B <= the cache's batch, 1 <= M <= 64. */
+spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                                const int32_t* n_tok, int B, int M, float* logits,
+                                int32_t* row_status, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* One draft step ([ZSM] "The algorithm": the draft generates K tokens autoregressively;
+ * [CANON] listing, draft loop; [LENS] §2.1 step 1): a forward of the draft model over
+ * this step's input tokens, then x~_step ~ q_step drawn by inverse CDF with the
+ * uniform U(seed, round, step, b, purpose 0) after the knobs (same transform as the
+ * rule).  Input tokens: step 0 takes in_tok[b, 0..n_in[b]-1] (in_tok [B,2], n_in [B]
+ * in {1,2}: the draft's pending tokens); step s > 0 takes x_tilde[b, s-1].
+ *   x_tilde  [B, K] int32, column `step` written
+ *   q_logits [B, K, V] fp32, row `step` written (the draft logits at the last input)
+ * A step-0 call records the row's pre-round cache length for spec_accept_resample. */
+spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t* in_tok,
+                            const int32_t* n_in, int B, int K, int step,
+                            const spec_sampling* knobs, uint64_t seed, uint64_t round,
+                            int32_t* x_tilde, float* q_logits, int32_t* row_status,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ the rule ------ */
+
+/* Workspace bytes for spec_accept_resample with B rows and K drafts. */
+size_t spec_accept_workspace_bytes(int B, int K);
+
+/* The modified rejection-sampling step for every row, evaluated data-parallel over
+ * positions with counter-based uniforms so that it equals the left-to-right walk:
+ *   accept x~_j  <=>  U(seed,round,j,b,1) * q_j(x~_j) < p_j(x~_j)
+ *     ([ZSM] "The algorithm", acceptance eq.; [CANON] eq. alpha(x); [LENS] §2.3;
+ *      written without division, equal to u < min(1, p/q) whenever q > 0)
+ *   a = number of leading accepts;
+ *   a < K : y ~ norm(max(0, p_a - q_a)) by inverse CDF with U(seed,round,a,b,2)
+ *     ([CANON] residual eq.; [LENS] §2.3 eq. p'); an all-zero residual samples p_a
+ *     instead (SPEC_ROW_RESIDUAL_EMPTY)
+ *   a = K : bonus y ~ p_K with U(seed,round,K,b,2) ([LENS] §2.1 step 3; [GC] step 4)
+ *   out_tok[b] = x~_0..x~_{a-1}, y (then -1 padding); n_out[b] = a + 1 in [1, K+1]
+ *     ([LENS] §2.1; [NOTE] "At least one token per loop").
+ * Uniforms: Philox4x64-10 (Salmon et al., SC'11), key (seed, 0), counter
+ * (round, j, b, purpose), u = top 24 bits of word 0 times 2^-24.
+ * Inverse CDF: smallest token id i whose running sum (token-id order) exceeds u * S.
+ *   p_logits [B, K+1, V] fp32, q_logits [B, K, V] fp32, x_tilde [B, K] int32
+ *   out_tok [B, K+1] int32 out, n_out [B] int32 out, row_status [B] int32 out (set)
+ * Optional state updates (NULL = skip):
+ *   tkv: target cache after the verify appended K+1 rows: len <- pre-verify len + a+1
+ *   dkv: draft cache after K draft steps: len <- target's new len if a < K, unchanged
+ *        if a = K
+ *   pending [B, 2] / n_pending [B]: the draft's pending tokens for the next round:
+ *        [y] if a < K, [x~_{K-1}, y] if a = K
+ * A row with NONFINITE, BAD_TOKEN or KV_OVERFLOW emits nothing (n_out = 0) and its
+ * caches are restored to their pre-round lengths.
+ * V <= 32768 (else SPEC_E_UNSUPPORTED); 1 <= K <= 16.
+ * `debug` (NULL = none) exports intermediate values for parity checks:
+ *   debug[0] float* p_probs [B, K+1, V], debug[1] float* q_probs [B, K, V],
+ *   debug[2] int32_t* accept [B, K], debug[3] int32_t* cand [B, K+1]
+ *   (cand[j] = the token position j would emit if it were the first rejection, or the
+ *   bonus token for j = K; -1 where not evaluated). */
+spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
+                                 const int32_t* x_tilde, int B, int K, int V,
+                                 const spec_sampling* knobs, uint64_t seed, uint64_t round,
+                                 int32_t* out_tok, int32_t* n_out, int32_t* row_status,
+                                 spec_kv* tkv, spec_kv* dkv, int32_t* pending,
+                                 int32_t* n_pending, void* const* debug, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ misc ---------- */
+
+const char* spec_status_str(int status);
+int spec_last_hip_error(void); /* hipError_t of the last failed launch (0 = none) */
+int spec_abi_version(void);    /* bumped on any incompatible change to this header  */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECDEC_H */

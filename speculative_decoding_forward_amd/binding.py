@@ -1,0 +1,228 @@
+"""ctypes binding of libspecdec.so: argument marshalling only.
+
+Every computation runs in the HIP library; this module converts torch tensors to device
+pointers, torch streams to hipStream_t handles, and status codes to exceptions.  There
+is no CPU fallback: if the library is missing, ``load()`` raises.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import synth
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecdec.so")
+
+SPEC_OK, SPEC_E_INVALID, SPEC_E_UNSUPPORTED, SPEC_E_CAPACITY, SPEC_E_HIP = 0, -1, -2, -3, -4
+ROW_NONFINITE, ROW_Q_ZERO, ROW_RESIDUAL_EMPTY, ROW_KV_OVERFLOW, ROW_BAD_TOKEN = 1, 2, 4, 8, 16
+FFN = {"gelu": 0, "swiglu": 1}
+DT = {"f32": 0, "bf16": 1}
+
+SYMBOLS = [
+    "spec_model_n_weights", "spec_model_create", "spec_model_destroy", "spec_kv_bytes",
+    "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_rollback",
+    "spec_workspace_bytes", "spec_verify_forward", "spec_draft_step",
+    "spec_accept_workspace_bytes", "spec_accept_resample", "spec_status_str",
+    "spec_last_hip_error", "spec_abi_version",
+]
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("d_model", ctypes.c_int),
+                ("n_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("d_ffn", ctypes.c_int), ("vocab", ctypes.c_int),
+                ("ffn_kind", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+    @classmethod
+    def from_shape(cls, s: "synth.ModelShape"):
+        return cls(s.n_layers, s.d_model, s.n_heads, s.head_dim, s.d_ffn, s.vocab,
+                   FFN[s.ffn_kind], DT[s.dtype], s.norm_eps, s.rope_theta)
+
+
+class Sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int),
+                ("top_p", ctypes.c_float)]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_LIB.spec_status_str(status).decode()} ({status})"
+                         + (f", hip error {_LIB.spec_last_hip_error()}"
+                            if status == SPEC_E_HIP else ""))
+
+
+_LIB = None
+P = ctypes.c_void_p
+I32 = ctypes.c_int
+U64 = ctypes.c_uint64
+SZ = ctypes.c_size_t
+
+
+def load(path=None):
+    """Load the library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m speculative_decoding_forward_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    cfgp = ctypes.POINTER(ModelCfg)
+    smp = ctypes.POINTER(Sampling)
+    sig = {
+        "spec_model_n_weights": (I32, [cfgp]),
+        "spec_model_create": (I32, [cfgp, ctypes.POINTER(P), I32, ctypes.POINTER(P)]),
+        "spec_model_destroy": (I32, [P]),
+        "spec_kv_bytes": (SZ, [cfgp, I32, I32]),
+        "spec_kv_create": (I32, [cfgp, I32, I32, P, SZ, P, ctypes.POINTER(P)]),
+        "spec_kv_destroy": (I32, [P]),
+        "spec_kv_data": (P, [P]),
+        "spec_kv_rollback": (I32, [P, P, P]),
+        "spec_workspace_bytes": (SZ, [cfgp, I32, I32, I32]),
+        "spec_verify_forward": (I32, [P, P, P, P, I32, I32, P, P, P, SZ, P]),
+        "spec_draft_step": (I32, [P, P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, SZ, P]),
+        "spec_accept_workspace_bytes": (SZ, [I32, I32]),
+        "spec_accept_resample": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P,
+                                       P, P, ctypes.POINTER(P), P, SZ, P]),
+        "spec_status_str": (ctypes.c_char_p, [I32]),
+        "spec_last_hip_error": (I32, []),
+        "spec_abi_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status, where):
+    if status != SPEC_OK:
+        raise SpecError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _alloc(nbytes, device):
+    """256-byte aligned device buffer (torch's allocator aligns to at least 512)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class Model:
+    """A model bound to device weights (dict name -> tensor, canonical order)."""
+
+    def __init__(self, shape: "synth.ModelShape", weights):
+        lib = load()
+        self.shape = shape
+        self.cfg = ModelCfg.from_shape(shape)
+        names = shape.weight_names()
+        self.weights = [weights[n].contiguous() for n in names]
+        arr = (P * len(names))(*[t.data_ptr() for t in self.weights])
+        h = P()
+        _check(lib.spec_model_create(ctypes.byref(self.cfg), arr, len(names), ctypes.byref(h)),
+               "spec_model_create")
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.spec_model_destroy(self.handle)
+            self.handle = None
+
+    def workspace(self, batch, max_rows, max_len, device="cuda"):
+        n = load().spec_workspace_bytes(ctypes.byref(self.cfg), batch, max_rows, max_len)
+        if n == 0:
+            raise SpecError(SPEC_E_INVALID, "spec_workspace_bytes")
+        return _alloc(n, device)
+
+
+class KVCache:
+    """A KV arena + lengths for `batch` rows of up to `max_len` positions."""
+
+    def __init__(self, shape: "synth.ModelShape", batch, max_len, device="cuda"):
+        lib = load()
+        self.shape = shape
+        self.cfg = ModelCfg.from_shape(shape)
+        self.batch, self.max_len = batch, max_len
+        n = lib.spec_kv_bytes(ctypes.byref(self.cfg), batch, max_len)
+        if n == 0:
+            raise SpecError(SPEC_E_INVALID, "spec_kv_bytes")
+        self.arena = _alloc(n, device)
+        self.len = torch.zeros(batch, dtype=torch.int32, device=device)
+        h = P()
+        _check(lib.spec_kv_create(ctypes.byref(self.cfg), batch, max_len, _ptr(self.arena), n,
+                                  _ptr(self.len), ctypes.byref(h)), "spec_kv_create")
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.spec_kv_destroy(self.handle)
+            self.handle = None
+
+    def data(self):
+        """The K/V block viewed as [L, B, 2, H, max_len, hd] (bf16 or fp32)."""
+        s = self.shape
+        dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+        n = s.n_layers * self.batch * 2 * s.n_heads * self.max_len * s.head_dim
+        flat = self.arena[: n * (2 if s.dtype == "bf16" else 4)].view(dt)
+        return flat.view(s.n_layers, self.batch, 2, s.n_heads, self.max_len, s.head_dim)
+
+    def rollback(self, new_len, stream=None):
+        _check(load().spec_kv_rollback(self.handle, _ptr(new_len), _stream(stream)),
+               "spec_kv_rollback")
+
+
+def verify_forward(model: Model, kv: KVCache, tokens, logits, ws, n_tok=None, row_status=None,
+                   stream=None):
+    """tokens [B, M] int32, logits [B, M, V] fp32 (out)."""
+    B, M = tokens.shape
+    _check(load().spec_verify_forward(model.handle, kv.handle, _ptr(tokens), _ptr(n_tok), B, M,
+                                      _ptr(logits), _ptr(row_status), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "spec_verify_forward")
+
+
+def draft_step(model: Model, kv: KVCache, in_tok, n_in, step, knobs, seed, rnd, x_tilde,
+               q_logits, ws, row_status=None, stream=None):
+    B, K = x_tilde.shape
+    smp = Sampling(*knobs)
+    _check(load().spec_draft_step(model.handle, kv.handle, _ptr(in_tok), _ptr(n_in), B, K, step,
+                                  ctypes.byref(smp), seed, rnd, _ptr(x_tilde), _ptr(q_logits),
+                                  _ptr(row_status), _ptr(ws), ws.numel(), _stream(stream)),
+           "spec_draft_step")
+
+
+def accept_workspace(B, K, device="cuda"):
+    return _alloc(load().spec_accept_workspace_bytes(B, K), device)
+
+
+def accept_resample(p_logits, q_logits, x_tilde, knobs, seed, rnd, out_tok, n_out, row_status,
+                    ws, tkv=None, dkv=None, pending=None, n_pending=None, debug=None,
+                    stream=None):
+    """p_logits [B, K+1, V], q_logits [B, K, V] fp32; x_tilde [B, K] int32.
+
+    debug: optional (p_probs, q_probs, accept, cand) tensors or None entries.
+    """
+    B, K1, V = p_logits.shape
+    K = K1 - 1
+    smp = Sampling(*knobs)
+    dbg = None
+    if debug is not None:
+        dbg = (P * 4)(*[(t.data_ptr() if t is not None else None) for t in debug])
+    _check(load().spec_accept_resample(
+        _ptr(p_logits), _ptr(q_logits), _ptr(x_tilde), B, K, V, ctypes.byref(smp), seed, rnd,
+        _ptr(out_tok), _ptr(n_out), _ptr(row_status), tkv.handle if tkv else None,
+        dkv.handle if dkv else None, _ptr(pending), _ptr(n_pending), dbg, _ptr(ws), ws.numel(),
+        _stream(stream)), "spec_accept_resample")

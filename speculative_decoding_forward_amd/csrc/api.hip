@@ -1,0 +1,382 @@
+// C ABI of the library (declared in include/specdec.h): argument checks, workspace
+// layout, and the launch sequence of the verify pass, the draft step and the rule.
+// Host code only; every step of the computation runs in the kernels of gemm.hip,
+// layers.hip and sampling.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+using namespace specdec;
+
+namespace {
+
+std::atomic<int> g_last_hip_error{0};
+
+spec_status hip_fail(hipError_t e) {
+  g_last_hip_error.store((int)e);
+  return SPEC_E_HIP;
+}
+
+#define SPEC_LAUNCH(expr)                     \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+inline size_t elt_bytes(const spec_model_cfg& c) { return c.dtype == SPEC_DT_BF16 ? 2 : 4; }
+
+bool cfg_valid(const spec_model_cfg* c) {
+  if (!c) return false;
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->head_dim < 2 ||
+      c->d_ffn < 1 || c->vocab < 1)
+    return false;
+  if (c->n_heads * c->head_dim != c->d_model) return false;
+  if (c->ffn_kind != SPEC_FFN_GELU && c->ffn_kind != SPEC_FFN_SWIGLU) return false;
+  if (c->dtype != SPEC_DT_F32 && c->dtype != SPEC_DT_BF16) return false;
+  if (!(c->norm_eps >= 0.f) || !(c->rope_theta > 0.f)) return false;
+  return true;
+}
+
+bool cfg_supported(const spec_model_cfg* c) {
+  if (c->dtype == SPEC_DT_BF16) {
+    if (c->head_dim != 64 && c->head_dim != 128) return false;
+    if (c->d_model % 16 || c->d_ffn % 16 || c->vocab % 16) return false;
+  } else {
+    if (c->head_dim % 2 || c->head_dim > 128) return false;
+  }
+  return true;
+}
+
+int g_device_ok = -1;  // -1 unknown, 0 no, 1 yes
+bool device_is_gfx950() {
+  if (g_device_ok >= 0) return g_device_ok == 1;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    g_device_ok = 0;
+    return false;
+  }
+  g_device_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  return g_device_ok == 1;
+}
+
+bool knobs_valid(const spec_sampling* k) {
+  if (!k) return false;
+  if (!(k->temperature >= 0.f) || !std::isfinite(k->temperature)) return false;
+  if (k->top_k < 0) return false;
+  if (!(k->top_p > 0.f && k->top_p <= 1.f)) return false;
+  return true;
+}
+
+SamplingKnobs to_knobs(const spec_sampling* k) {
+  return SamplingKnobs{1.0f / k->temperature, k->top_k, k->top_p};
+}
+
+// Workspace of the forward: regions carved from the caller's buffer.
+struct FwdWS {
+  int32_t* pos0;
+  int32_t* ntok_eff;
+  int32_t* tok_eff;
+  int32_t* tok2;    // draft-step input tokens [B, 2]
+  int32_t* ntok2;   // draft-step counts [B]
+  float* x;         // residual stream [R, d]
+  void* h;          // normed activations [R, d]
+  void* a;          // FFN activations [R, F]
+  float* y;         // GEMM outputs [R, max(3d, 2F)]
+  void* q;          // rotated queries [R, d]
+  void* att;        // attention output [R, d]
+  float* part;      // attention partials
+  float* logits;    // draft-step logits [R, V]
+  size_t total;
+};
+
+FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base) {
+  FwdWS w{};
+  const size_t R = (size_t)B * M;
+  const size_t e = elt_bytes(c);
+  const size_t d = c.d_model, F = c.d_ffn, V = c.vocab;
+  const size_t ffn_out = c.ffn_kind == SPEC_FFN_SWIGLU ? 2 * F : F;
+  const size_t nsplit = (size_t)cdiv(max_len, attn_chunk());
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.pos0 = (int32_t*)take(B * 4);
+  w.ntok_eff = (int32_t*)take(B * 4);
+  w.tok_eff = (int32_t*)take(R * 4);
+  w.tok2 = (int32_t*)take((size_t)B * 2 * 4);
+  w.ntok2 = (int32_t*)take(B * 4);
+  w.x = (float*)take(R * d * 4);
+  w.h = take(R * d * e);
+  w.a = take(R * F * e);
+  w.y = (float*)take(R * std::max(3 * d, ffn_out) * 4);
+  w.q = take(R * d * e);
+  w.att = take(R * d * e);
+  w.part = (float*)take((size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4);
+  w.logits = (float*)take(R * V * 4);
+  w.total = off;
+  return w;
+}
+
+// The forward pass shared by the verify call, draft steps and prefill chunks.
+spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                    const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
+                    int record_base, const FwdWS& w, hipStream_t s) {
+  const spec_model_cfg& c = m->cfg;
+  const int dt = c.dtype;
+  const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
+            hd = c.head_dim;
+  const size_t e = elt_bytes(c);
+  const int nsplit = cdiv(kv->max_len, attn_chunk());
+  SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, V, kv->len, kv->base, record_base, kv->max_len,
+                          w.pos0, w.ntok_eff, w.tok_eff, row_status, s));
+  SPEC_LAUNCH(launch_embed(m->embed, dt, w.tok_eff, R, d, w.x, s));
+  const int swiglu = c.ffn_kind == SPEC_FFN_SWIGLU;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const spec_model::Layer& L = m->layers[l];
+    char* kl = (char*)kv->data + (size_t)l * kv->layer_stride * e;
+    char* vl = kl + kv->kv_stride * e;
+    SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm1, R, d, c.norm_eps, dt, w.h, s));
+    SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.wqkv, nullptr, R, 3 * d, 3 * d, d, w.y, 0, nullptr, 0, s));
+    SPEC_LAUNCH(launch_rope_append(dt, w.y, B, M, H, hd, c.rope_theta, w.pos0, w.ntok_eff, w.q,
+                                   kl, vl, kv->row_stride, kv->head_stride, kv->max_len, s));
+    SPEC_LAUNCH(launch_attention(dt, w.q, kl, vl, kv->row_stride, kv->head_stride, B, M, H, hd,
+                                 w.pos0, w.ntok_eff, w.part, nsplit, kv->max_len, w.att, s));
+    SPEC_LAUNCH(launch_gemm_ex(dt, w.att, L.wo, nullptr, R, d, d, d, w.x, 1, nullptr, 0, s));
+    SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm2, R, d, c.norm_eps, dt, w.h, s));
+    if (swiglu) {
+      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, L.w_up2, R, 2 * F, F, d, w.y, 0, nullptr, 0, s));
+    } else {
+      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, nullptr, R, F, F, d, w.y, 0, nullptr, 0, s));
+    }
+    SPEC_LAUNCH(launch_act(dt, c.ffn_kind, w.y, R, F, w.a, s));
+    SPEC_LAUNCH(launch_gemm_ex(dt, w.a, L.w_down, nullptr, R, d, d, F, w.x, 1, nullptr, 0, s));
+  }
+  SPEC_LAUNCH(launch_rmsnorm(w.x, m->norm_f, R, d, c.norm_eps, dt, w.h, s));
+  SPEC_LAUNCH(launch_gemm_ex(dt, w.h, m->head, nullptr, R, V, V, d, logits, 0, w.ntok_eff, M, s));
+  return SPEC_OK;
+}
+
+bool kv_matches(const spec_model* m, const spec_kv* kv) {
+  const spec_model_cfg &a = m->cfg, &b = kv->cfg;
+  return a.n_layers == b.n_layers && a.n_heads == b.n_heads && a.head_dim == b.head_dim &&
+         a.dtype == b.dtype;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_abi_version(void) { return 1; }
+
+int spec_last_hip_error(void) { return g_last_hip_error.load(); }
+
+const char* spec_status_str(int st) {
+  switch (st) {
+    case SPEC_OK: return "ok";
+    case SPEC_E_INVALID: return "invalid argument";
+    case SPEC_E_UNSUPPORTED: return "unsupported";
+    case SPEC_E_CAPACITY: return "buffer too small";
+    case SPEC_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int spec_model_n_weights(const spec_model_cfg* cfg) {
+  if (!cfg_valid(cfg)) return -1;
+  return 3 + cfg->n_layers * (cfg->ffn_kind == SPEC_FFN_SWIGLU ? 7 : 6);
+}
+
+spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
+                              int n_weights, spec_model** out) {
+  if (!cfg_valid(cfg) || !weights || !out) return SPEC_E_INVALID;
+  if (n_weights != spec_model_n_weights(cfg)) return SPEC_E_INVALID;
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i]) return SPEC_E_INVALID;
+  if (!cfg_supported(cfg)) return SPEC_E_UNSUPPORTED;
+  if (!device_is_gfx950()) return SPEC_E_UNSUPPORTED;
+  spec_model* m = new (std::nothrow) spec_model;
+  if (!m) return SPEC_E_INVALID;
+  m->cfg = *cfg;
+  m->layers = new (std::nothrow) spec_model::Layer[cfg->n_layers];
+  if (!m->layers) {
+    delete m;
+    return SPEC_E_INVALID;
+  }
+  int i = 0;
+  m->embed = weights[i++];
+  m->head = weights[i++];
+  m->norm_f = (const float*)weights[i++];
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    spec_model::Layer& L = m->layers[l];
+    L.norm1 = (const float*)weights[i++];
+    L.wqkv = weights[i++];
+    L.wo = weights[i++];
+    L.norm2 = (const float*)weights[i++];
+    if (cfg->ffn_kind == SPEC_FFN_SWIGLU) {
+      L.w_up = weights[i++];
+      L.w_up2 = weights[i++];
+      L.w_down = weights[i++];
+    } else {
+      L.w_up = weights[i++];
+      L.w_up2 = nullptr;
+      L.w_down = weights[i++];
+    }
+  }
+  *out = m;
+  return SPEC_OK;
+}
+
+spec_status spec_model_destroy(spec_model* m) {
+  if (!m) return SPEC_E_INVALID;
+  delete[] m->layers;
+  delete m;
+  return SPEC_OK;
+}
+
+size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len) {
+  if (!cfg_valid(cfg) || batch < 1 || max_len < 1) return 0;
+  const size_t n = (size_t)cfg->n_layers * batch * 2 * cfg->n_heads * max_len * cfg->head_dim;
+  return align_up(n * elt_bytes(*cfg)) + align_up((size_t)batch * 4);
+}
+
+spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, void* arena,
+                           size_t arena_bytes, int32_t* len, spec_kv** out) {
+  if (!cfg_valid(cfg) || batch < 1 || max_len < 1 || !arena || !len || !out)
+    return SPEC_E_INVALID;
+  if (((uintptr_t)arena) % 256) return SPEC_E_INVALID;
+  if (arena_bytes < spec_kv_bytes(cfg, batch, max_len)) return SPEC_E_CAPACITY;
+  spec_kv* kv = new (std::nothrow) spec_kv;
+  if (!kv) return SPEC_E_INVALID;
+  kv->cfg = *cfg;
+  kv->batch = batch;
+  kv->max_len = max_len;
+  kv->data = arena;
+  kv->len = len;
+  const size_t hd = cfg->head_dim, H = cfg->n_heads;
+  kv->head_stride = (size_t)max_len * hd;
+  kv->kv_stride = H * kv->head_stride;
+  kv->row_stride = 2 * kv->kv_stride;
+  kv->layer_stride = (size_t)batch * kv->row_stride;
+  const size_t n = (size_t)cfg->n_layers * kv->layer_stride;
+  kv->base = (int32_t*)((char*)arena + align_up(n * elt_bytes(*cfg)));
+  *out = kv;
+  return SPEC_OK;
+}
+
+spec_status spec_kv_destroy(spec_kv* kv) {
+  if (!kv) return SPEC_E_INVALID;
+  delete kv;
+  return SPEC_OK;
+}
+
+void* spec_kv_data(spec_kv* kv) { return kv ? kv->data : nullptr; }
+
+spec_status spec_kv_rollback(spec_kv* kv, const int32_t* new_len, void* stream) {
+  if (!kv || !new_len) return SPEC_E_INVALID;
+  SPEC_LAUNCH(launch_rollback(kv->len, new_len, kv->batch, (hipStream_t)stream));
+  return SPEC_OK;
+}
+
+size_t spec_workspace_bytes(const spec_model_cfg* cfg, int batch, int max_rows, int max_len) {
+  if (!cfg_valid(cfg) || batch < 1 || max_rows < 1 || max_len < 1) return 0;
+  return fwd_layout(*cfg, batch, std::max(max_rows, 2), max_len, nullptr).total;
+}
+
+spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                                const int32_t* n_tok, int B, int M, float* logits,
+                                int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !kv || !tokens || !logits || !ws) return SPEC_E_INVALID;
+  if (B < 1 || B > kv->batch || M < 1 || M > 64) return SPEC_E_INVALID;
+  if (!kv_matches(m, kv)) return SPEC_E_INVALID;
+  if (((uintptr_t)ws) % 256) return SPEC_E_INVALID;
+  const FwdWS w = fwd_layout(m->cfg, B, M, kv->max_len, (char*)ws);
+  if (ws_bytes < w.total) return SPEC_E_CAPACITY;
+  return forward(m, kv, tokens, n_tok, B, M, logits, row_status, 1, w, (hipStream_t)stream);
+}
+
+spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t* in_tok,
+                            const int32_t* n_in, int B, int K, int step,
+                            const spec_sampling* knobs, uint64_t seed, uint64_t round,
+                            int32_t* x_tilde, float* q_logits, int32_t* row_status, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!draft || !dkv || !x_tilde || !q_logits || !ws || !knobs_valid(knobs))
+    return SPEC_E_INVALID;
+  if (B < 1 || B > dkv->batch || K < 1 || K > 16 || step < 0 || step >= K)
+    return SPEC_E_INVALID;
+  if (step == 0 && (!in_tok || !n_in)) return SPEC_E_INVALID;
+  if (!kv_matches(draft, dkv)) return SPEC_E_INVALID;
+  if (knobs->temperature == 0.f) return SPEC_E_UNSUPPORTED;
+  if (draft->cfg.vocab > 32768) return SPEC_E_UNSUPPORTED;
+  if (((uintptr_t)ws) % 256) return SPEC_E_INVALID;
+  const int M = step == 0 ? 2 : 1;
+  const FwdWS w = fwd_layout(draft->cfg, B, M, dkv->max_len, (char*)ws);
+  if (ws_bytes < w.total) return SPEC_E_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  SPEC_LAUNCH(launch_draft_tokens(in_tok, n_in, x_tilde, B, K, step, w.tok2, w.ntok2, s));
+  spec_status st =
+      forward(draft, dkv, w.tok2, w.ntok2, B, M, w.logits, row_status, step == 0 ? 1 : 0, w, s);
+  if (st != SPEC_OK) return st;
+  SPEC_LAUNCH(launch_draft_sample(w.logits, B, M, w.ntok2, step, K, draft->cfg.vocab,
+                                  to_knobs(knobs), seed, round, x_tilde, q_logits, s));
+  return SPEC_OK;
+}
+
+size_t spec_accept_workspace_bytes(int B, int K) {
+  if (B < 1 || K < 1) return 0;
+  return align_up((size_t)B * K * 4) + 2 * align_up((size_t)B * (K + 1) * 4);
+}
+
+spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
+                                 const int32_t* x_tilde, int B, int K, int V,
+                                 const spec_sampling* knobs, uint64_t seed, uint64_t round,
+                                 int32_t* out_tok, int32_t* n_out, int32_t* row_status,
+                                 spec_kv* tkv, spec_kv* dkv, int32_t* pending,
+                                 int32_t* n_pending, void* const* debug, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!p_logits || !q_logits || !x_tilde || !out_tok || !n_out || !row_status || !ws)
+    return SPEC_E_INVALID;
+  if (B < 1 || K < 1 || K > 16 || V < 1 || !knobs_valid(knobs)) return SPEC_E_INVALID;
+  if ((pending == nullptr) != (n_pending == nullptr)) return SPEC_E_INVALID;
+  if (tkv && tkv->batch < B) return SPEC_E_INVALID;
+  if (dkv && dkv->batch < B) return SPEC_E_INVALID;
+  if (knobs->temperature == 0.f) return SPEC_E_UNSUPPORTED;
+  if (V > 32768) return SPEC_E_UNSUPPORTED;
+  if (ws_bytes < spec_accept_workspace_bytes(B, K)) return SPEC_E_CAPACITY;
+  char* p = (char*)ws;
+  int32_t* res_acc = (int32_t*)p;
+  p += align_up((size_t)B * K * 4);
+  int32_t* res_cand = (int32_t*)p;
+  p += align_up((size_t)B * (K + 1) * 4);
+  int32_t* res_status = (int32_t*)p;
+  float* dbg_p = debug ? (float*)debug[0] : nullptr;
+  float* dbg_q = debug ? (float*)debug[1] : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  SPEC_LAUNCH(launch_accept_rows(p_logits, q_logits, x_tilde, B, K, V, to_knobs(knobs), seed,
+                                 round, res_acc, res_cand, res_status, dbg_p, dbg_q, s));
+  SPEC_LAUNCH(launch_select(x_tilde, B, K, res_acc, res_cand, res_status, out_tok, n_out,
+                            row_status, tkv ? tkv->len : nullptr, tkv ? tkv->base : nullptr,
+                            dkv ? dkv->len : nullptr, dkv ? dkv->base : nullptr, pending,
+                            n_pending, s));
+  if (debug && debug[2])
+    SPEC_LAUNCH(hipMemcpyAsync(debug[2], res_acc, (size_t)B * K * 4, hipMemcpyDeviceToDevice, s));
+  if (debug && debug[3])
+    SPEC_LAUNCH(hipMemcpyAsync(debug[3], res_cand, (size_t)B * (K + 1) * 4,
+                               hipMemcpyDeviceToDevice, s));
+  return SPEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Host-side structures shared by the C ABI implementation and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specdec.h"
+
+struct spec_model {
+  spec_model_cfg cfg;
+  // device pointers, canonical order (see spec_model_create)
+  const void* embed;
+  const void* head;
+  const float* norm_f;
+  struct Layer {
+    const float* norm1;
+    const void* wqkv;
+    const void* wo;
+    const float* norm2;
+    const void* w_up;    // SwiGLU: wgate; GELU: w1
+    const void* w_up2;   // SwiGLU: wup;   GELU: unused
+    const void* w_down;  // SwiGLU: wdown; GELU: w2
+  };
+  Layer* layers;
+};
+
+struct spec_kv {
+  spec_model_cfg cfg;
+  int batch, max_len;
+  void* data;        // [L][B][2][H][max_len][hd]
+  int32_t* len;      // [B] caller-owned
+  int32_t* base;     // [B] length before the last recorded append (in the arena tail)
+  size_t layer_stride, row_stride, kv_stride, head_stride;  // in elements
+};
+
+struct SamplingKnobs {
+  float inv_t;
+  int top_k;
+  float top_p;
+};
+
+// kernel launchers (defined in the .hip files)
+namespace specdec {
+
+// forward pieces
+hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,
+                       int32_t* len, int32_t* base, int record_base, int max_len,
+                       int32_t* pos0, int32_t* ntok_eff, int32_t* tok_eff,
+                       int32_t* row_status, hipStream_t s);
+hipError_t launch_embed(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
+                        float* x, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, const float* g, int R, int d, float eps,
+                          int dtype, void* h, hipStream_t s);
+// C[R, N] (+)= A[R, K] W[N, K]^T; rows n >= N1 come from W2 (row n - N1); rows r with
+// r % rows_per_seq >= ntok_eff[r / rows_per_seq] are stored as 0 when ntok_eff is set.
+hipError_t launch_gemm_ex(int dtype, const void* A, const void* W, const void* W2, int R,
+                          int N, int N1, int K, float* C, int accumulate,
+                          const int32_t* ntok_eff, int rows_per_seq, hipStream_t s);
+hipError_t launch_rope_append(int dtype, const float* qkv, int B, int M, int H, int hd,
+                              float theta, const int32_t* pos0, const int32_t* ntok_eff,
+                              void* q_out, void* kcache, void* vcache, size_t row_stride,
+                              size_t head_stride, int max_len, hipStream_t s);
+hipError_t launch_attention(int dtype, const void* q, const void* kcache, const void* vcache,
+                            size_t row_stride, size_t head_stride, int B, int M, int H, int hd,
+                            const int32_t* pos0, const int32_t* ntok_eff, float* part,
+                            int n_split_max, int max_len, void* out, hipStream_t s);
+int attn_chunk();  // cache positions per attention split
+hipError_t launch_act(int dtype, int ffn_kind, const float* y, int R, int F, void* a,
+                      hipStream_t s);
+
+// sampling
+hipError_t launch_accept_rows(const float* p_logits, const float* q_logits,
+                              const int32_t* x_tilde, int B, int K, int V, SamplingKnobs kn,
+                              uint64_t seed, uint64_t round, int32_t* res_acc,
+                              int32_t* res_cand, int32_t* res_status, float* dbg_p,
+                              float* dbg_q, hipStream_t s);
+hipError_t launch_select(const int32_t* x_tilde, int B, int K, const int32_t* res_acc,
+                         const int32_t* res_cand, const int32_t* res_status,
+                         int32_t* out_tok, int32_t* n_out, int32_t* row_status,
+                         int32_t* t_len, const int32_t* t_base, int32_t* d_len,
+                         const int32_t* d_base, int32_t* pending, int32_t* n_pending,
+                         hipStream_t s);
+hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t* n_in,
+                               int step, int K, int V, SamplingKnobs kn, uint64_t seed,
+                               uint64_t round, int32_t* x_tilde, float* q_logits,
+                               hipStream_t s);
+hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
+                               const int32_t* x_tilde, int B, int K, int step,
+                               int32_t* tokens, int32_t* n_tok, hipStream_t s);
+hipError_t launch_rollback(int32_t* len, const int32_t* new_len, int B, hipStream_t s);
+
+}  // namespace specdec

@@ -1,0 +1,82 @@
+"""The C-ABI library loads and exports every entry point include/specdec.h declares;
+host-side size queries and argument checks (no kernel launches, no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_forward_amd import binding, synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "specdec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(binding.SYMBOLS)
+
+
+def test_abi_version_and_status_strings():
+    lib = binding.load()
+    assert lib.spec_abi_version() == 1
+    assert lib.spec_status_str(0) == b"ok"
+    assert lib.spec_status_str(-3) == b"buffer too small"
+
+
+def test_size_queries():
+    lib = binding.load()
+    s = synth.WORKLOADS["7b"].target
+    cfg = binding.ModelCfg.from_shape(s)
+    assert lib.spec_model_n_weights(ctypes.byref(cfg)) == 3 + 7 * 32
+    g = synth.WORKLOADS["small"].target
+    cg = binding.ModelCfg.from_shape(g)
+    assert lib.spec_model_n_weights(ctypes.byref(cg)) == 3 + 6 * 24
+    kvb = lib.spec_kv_bytes(ctypes.byref(cfg), 8, 2112)
+    assert kvb >= 32 * 8 * 2 * 32 * 2112 * 128 * 2
+    assert kvb % 256 == 0
+    ws = lib.spec_workspace_bytes(ctypes.byref(cfg), 8, 6, 2112)
+    assert 48 * 32000 * 4 < ws < 512 * 2**20
+    assert lib.spec_accept_workspace_bytes(32, 8) >= 32 * 8 * 4 + 2 * 32 * 9 * 4
+    bad = binding.ModelCfg.from_shape(s)
+    bad.n_heads = 31
+    assert lib.spec_model_n_weights(ctypes.byref(bad)) == -1
+    assert lib.spec_kv_bytes(ctypes.byref(bad), 1, 16) == 0
+
+
+def test_argument_checks_launch_nothing():
+    lib = binding.load()
+    smp = binding.Sampling(1.0, 0, 1.0)
+    # null pointers -> invalid, before any launch
+    st = lib.spec_accept_resample(None, None, None, 1, 1, 10, ctypes.byref(smp), 0, 0, None,
+                                  None, None, None, None, None, None, None, None, 0, None)
+    assert st == binding.SPEC_E_INVALID
+    assert lib.spec_verify_forward(None, None, None, None, 1, 1, None, None, None, 0,
+                                   None) == binding.SPEC_E_INVALID
+    assert lib.spec_kv_rollback(None, None, None) == binding.SPEC_E_INVALID
+    assert lib.spec_model_destroy(None) == binding.SPEC_E_INVALID
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        binding.load.__wrapped__(str(tmp_path / "missing.so")) if hasattr(
+            binding.load, "__wrapped__") else _load_missing(tmp_path)
+
+
+def _load_missing(tmp_path):
+    saved = binding._LIB
+    binding._LIB = None
+    try:
+        binding.load(str(tmp_path / "missing.so"))
+    finally:
+        binding._LIB = saved

@@ -1,0 +1,162 @@
+"""GPU parity of spec_verify_forward (the verify pass) against the oracle forward.
+
+Tolerances: logits within 1e-4 abs for fp32 models and 1e-2 abs for bf16 models (fp32
+accumulation).  Cache contents of the appended positions are compared too.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as omodel
+from speculative_decoding_forward_amd import binding, synth
+
+from helpers import DEV, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_micro(kind, hd=128, L=2, d=256, F=512, V=1024):
+    return synth.ModelShape(n_layers=L, d_model=d, n_heads=d // hd, head_dim=hd, d_ffn=F,
+                            vocab=V, ffn_kind=kind, dtype="bf16")
+
+
+def setup(shape, seed=0, model_id=synth.TARGET):
+    Wd = synth.make_weights(shape, seed=seed, model_id=model_id, device=DEV)
+    Wn = synth.weights_to_numpy(Wd)
+    return binding.Model(shape, Wd), Wn
+
+
+def gpu_forward(m, kv, tokens, n_tok=None, max_len=None):
+    B, M = tokens.shape
+    ws = m.workspace(B, M, kv.max_len)
+    logits = torch.full((B, M, m.shape.vocab), 7.0, dtype=torch.float32, device=DEV)
+    st = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nt = None if n_tok is None else to_dev(np.asarray(n_tok, np.int32))
+    binding.verify_forward(m, kv, to_dev(tokens.astype(np.int32)), logits, ws, n_tok=nt,
+                           row_status=st)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), st.cpu().numpy()
+
+
+def prefill_both(m, kv, Wn, shape, ctx, chunk, oc):
+    """Feed ctx[:, :n] through the GPU in chunks and through the oracle."""
+    B, n = ctx.shape
+    for s in range(0, n, chunk):
+        gpu_forward(m, kv, ctx[:, s:s + chunk])
+    omodel.forward(shape, Wn, oc, ctx)
+
+
+@pytest.mark.parametrize("name", ["tiny_target", "tiny_draft"])
+def test_fp32_tiny_prefill_then_verify(name):
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.target if name == "tiny_target" else wl.draft
+    m, Wn = setup(shape, model_id=synth.TARGET if name == "tiny_target" else synth.DRAFT)
+    B, max_len = 2, 96
+    kv = binding.KVCache(shape, B, max_len)
+    oc = omodel.KVCache(shape, B, max_len)
+    ctx = synth.context_ids(0, B, wl.ctx - 1, shape.vocab)
+    prefill_both(m, kv, Wn, shape, ctx, 7, oc)
+    assert np.array_equal(kv.len.cpu().numpy(), oc.len)
+    new = synth.context_ids(1, B, wl.K + 1, shape.vocab)
+    g, st = gpu_forward(m, kv, new)
+    o = omodel.forward(shape, Wn, oc, new)
+    err = np.abs(g - o).max()
+    print(f"{name}: max |logit diff| = {err:.3e}")
+    assert err <= 1e-4
+    assert np.all(st == 0)
+    assert np.array_equal(kv.len.cpu().numpy(), oc.len)
+    # cache contents of every written position
+    data = kv.data().cpu().numpy()
+    for l in range(shape.n_layers):
+        for b in range(B):
+            n = oc.len[b]
+            np.testing.assert_allclose(data[l, b, 0, :, :n], oc.k[l][b, :, :n], atol=1e-5)
+            np.testing.assert_allclose(data[l, b, 1, :, :n], oc.v[l][b, :, :n], atol=1e-5)
+
+
+@pytest.mark.parametrize("kind,hd", [("swiglu", 128), ("gelu", 128), ("swiglu", 64)])
+def test_bf16_micro_ragged(kind, hd):
+    """bf16 with cache lengths crossing several 64-position attention chunks, ragged
+    rows (n_tok 6, 3, 0) and a prefill chunk of 64 tokens."""
+    shape = bf16_micro(kind, hd=hd)
+    m, Wn = setup(shape, seed=3)
+    B, max_len = 3, 256
+    kv = binding.KVCache(shape, B, max_len)
+    oc = omodel.KVCache(shape, B, max_len)
+    ctx = synth.context_ids(2, B, 150, shape.vocab)
+    prefill_both(m, kv, Wn, shape, ctx, 64, oc)
+    new = synth.context_ids(3, B, 6, shape.vocab)
+    n_tok = [6, 3, 0]
+    g, st = gpu_forward(m, kv, new, n_tok=n_tok)
+    o = omodel.forward(shape, Wn, oc, new, n_tok=n_tok)
+    for b in range(B):
+        n = n_tok[b]
+        if n:
+            err = np.abs(g[b, :n] - o[b, :n]).max()
+            print(f"{kind} hd={hd} row {b}: max |logit diff| = {err:.3e}")
+            assert err <= 1e-2
+        assert np.all(g[b, n:] == 0)
+    assert np.array_equal(kv.len.cpu().numpy(), oc.len)
+    data = kv.data().float().cpu().numpy()
+    for b in range(B):
+        s0, n = 150, n_tok[b]
+        for l in range(shape.n_layers):
+            kd = data[l, b, 0, :, s0:s0 + n]
+            ko = oc.k[l][b, :, s0:s0 + n]
+            assert np.abs(kd - ko).max() <= 2 ** -7 * max(1.0, np.abs(ko).max())
+
+
+def test_overflow_and_bad_tokens_flagged():
+    shape = bf16_micro("swiglu")
+    m, Wn = setup(shape, seed=4)
+    B, max_len = 3, 40
+    kv = binding.KVCache(shape, B, max_len)
+    ctx = synth.context_ids(4, B, 36, shape.vocab)
+    gpu_forward(m, kv, ctx)
+    new = synth.context_ids(5, B, 4, shape.vocab)
+    new[2, 1] = shape.vocab + 3
+    g, st = gpu_forward(m, kv, new, n_tok=[4, 5 - 1, 4])
+    assert np.all(st[:2] == 0) and st[2] & binding.ROW_BAD_TOKEN
+    # now every row is full: a further token overflows and is skipped
+    g, st = gpu_forward(m, kv, new[:, :1])
+    assert np.all(st & binding.ROW_KV_OVERFLOW)
+    assert np.all(g == 0)
+    assert np.array_equal(kv.len.cpu().numpy(), [40, 40, 40])
+
+
+def test_rollback():
+    shape = bf16_micro("gelu")
+    m, _ = setup(shape, seed=5)
+    kv = binding.KVCache(shape, 2, 64)
+    gpu_forward(m, kv, synth.context_ids(6, 2, 10, shape.vocab))
+    kv.rollback(to_dev(np.array([4, 20], np.int32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(kv.len.cpu().numpy(), [4, 10])
+
+
+def synthetic_kv_case(wl_name, B, K, seed=0):
+    """Full-size verify pass on a cache filled with seeded values (standing in for a
+    prefilled context of the workload's length), compared with the oracle."""
+    wl = synth.WORKLOADS[wl_name]
+    shape = wl.target
+    m, Wn = setup(shape, seed=seed)
+    max_len = wl.ctx + K + 1
+    kv = binding.KVCache(shape, B, max_len)
+    fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=seed, device=DEV)
+    kv.data().copy_(fill)
+    kv.len.fill_(wl.ctx)
+    oc = omodel.KVCache(shape, B, max_len)
+    oc.fill(fill.float().cpu().numpy(), [wl.ctx] * B)
+    del fill
+    new = synth.context_ids(seed + 9, B, K + 1, shape.vocab)
+    g, st = gpu_forward(m, kv, new)
+    o = omodel.forward(shape, Wn, oc, new)
+    return g, o, st
+
+
+def test_small_model_full_size():
+    """24-layer d=2048 GELU bf16 target, context 512, K=4, B=1."""
+    g, o, st = synthetic_kv_case("small", 1, 4)
+    err = np.abs(g - o).max()
+    print(f"small: max |logit diff| = {err:.3e}, logit scale {np.abs(o).max():.2f}")
+    assert err <= 1e-2 and np.all(st == 0)
