@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: speculative rounds on the 7B-shape bf16 workload, one MI355X.
+
+A timed step is one full speculative round over the batch: K draft steps, verify-input
+assembly, ONE target verify pass over K+1 positions, and the fused accept / resample /
+bonus step with cache roll-back.  Inputs are synthetic and seeded: random-init weights
+of the named shapes (N(0, 0.02^2), bf16), context ids uniform over the vocabulary,
+prefilled through the library before timing.  All inputs are resident in HBM when the
+timed region starts.
+
+Output: one JSON line.  value = emitted tokens per second over the whole job (accepted
+drafts plus the resampled or bonus token of every row, summed over rows).  The
+roofline object covers the dominant kernel (the weight-streaming GEMM), timed live with
+HIP events on its launch stream over the timed rounds.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="7b", choices=["tiny", "small", "7b", "70b"])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--K", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def gemm_bytes_per_verify(shape, R):
+    """Algorithmic bytes of the weight GEMMs of one forward over R rows: every weight
+    once, the activation rows read, the fp32 outputs written (read too when added)."""
+    d, F, V, L = shape.d_model, shape.d_ffn, shape.vocab, shape.n_layers
+    e = shape.elt_bytes()
+    ffn_in = 2 * F if shape.ffn_kind == "swiglu" else F
+    gemms = [(3 * d, d, 0), (d, d, 1), (ffn_in, d, 0), (d, F, 1)]  # (N, K, accumulate)
+    total, n = 0, 0
+    for N, K, acc in gemms:
+        total += L * (N * K * e + R * K * e + R * N * 4 * (2 if acc else 1))
+        n += L
+    total += V * d * e + R * d * e + R * V * 4
+    n += 1
+    return total, n
+
+
+def verify_bytes(shape, B, K, lens):
+    """Algorithmic bytes of one verify call: weights once, gathered embedding rows, KV
+    read (context + new positions) and write, logits."""
+    d, L = shape.d_model, shape.n_layers
+    e = shape.elt_bytes()
+    M = B * (K + 1)
+    w = shape.n_params() - shape.vocab * d      # all weights but the embedding table
+    w_bytes = w * e - (2 * L + 1) * d * (e - 4)  # norm gains are fp32
+    kv_read = sum(L * 2 * (int(l) + K + 1) * d * e for l in lens)
+    kv_write = B * L * 2 * (K + 1) * d * e
+    return w_bytes + M * d * e + kv_read + kv_write + M * shape.vocab * 4
+
+
+def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
+    """The oracle (numpy, float64) timed on this host on a bounded sample of the same
+    workload: one round's work for the first layer of the target and of the draft (per
+    layer cost), the LM heads and the accept step, scaled to the full depth."""
+    import dataclasses
+
+    import torch
+
+    from oracle import model as omodel
+    from oracle import philox, sampling
+    from speculative_decoding_forward_amd import synth
+
+    t_shape = dataclasses.replace(wl.target, n_layers=1)
+    d_shape = dataclasses.replace(wl.draft, n_layers=1)
+    Wt = synth.weights_to_numpy(synth.make_weights(t_shape, seed=0, device="cpu"))
+    Wd = synth.weights_to_numpy(synth.make_weights(d_shape, seed=0, model_id=1, device="cpu"))
+    ctx = wl.ctx
+
+    def cache(shape):
+        c = omodel.KVCache(shape, 1, ctx + K + 2)
+        fill = synth.kv_fill(shape, 1, ctx + K + 2, ctx, seed=0).float().numpy()
+        c.fill(fill, [ctx])
+        return c
+
+    tc, dc = cache(t_shape), cache(d_shape)
+    rng = np.random.default_rng(0)
+    new = rng.integers(0, wl.target.vocab, (1, K + 1))
+    reps, t_target, t_draft, t_acc = 0, 0.0, 0.0, 0.0
+    t_start = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t_start < target_seconds:
+        tc.len[:] = ctx
+        dc.len[:] = ctx
+        t0 = time.perf_counter()
+        plog = omodel.forward(t_shape, Wt, tc, new)
+        t1 = time.perf_counter()
+        qlog = np.concatenate([omodel.forward(d_shape, Wd, dc, new[:, j:j + 1])
+                               for j in range(K)], axis=1)
+        t2 = time.perf_counter()
+        sampling.accept_resample_logits(
+            plog[0].astype(np.float32), qlog[0].astype(np.float32), new[0, :K],
+            philox.uniform(0, reps, np.arange(K), 0, 1),
+            philox.uniform(0, reps, np.arange(K + 1), 0, 2), wl.temperature, wl.top_k,
+            wl.top_p)
+        t3 = time.perf_counter()
+        t_target += t1 - t0
+        t_draft += t2 - t1
+        t_acc += t3 - t2
+        reps += 1
+    t_target, t_draft, t_acc = t_target / reps, t_draft / reps, t_acc / reps
+    # a 1-layer forward = embed + 1 layer + head; scale the layer part by depth using a
+    # head-only estimate (the layer count only multiplies the per-layer work)
+    t0 = time.perf_counter()
+    omodel.forward(t_shape, Wt, tc, new, layers=0)
+    th = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for j in range(K):
+        omodel.forward(d_shape, Wd, dc, new[:, j:j + 1], layers=0)
+    dh = time.perf_counter() - t0
+    round_1row = ((t_target - th) * wl.target.n_layers + th +
+                  (t_draft - dh) * wl.draft.n_layers + dh + t_acc)
+    round_s = round_1row * B
+    cores = len(os.sched_getaffinity(0))
+    value = tokens_per_round / round_s
+    return {
+        "value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{reps} repetitions of one round's work on 1 target layer + 1 draft "
+                   f"layer (+ heads, accept step) at context {ctx}, K={K}, one row; "
+                   f"per-layer time scaled to {wl.target.n_layers}+{wl.draft.n_layers} "
+                   f"layers and {B} rows; numpy float64 with its default BLAS threads; "
+                   f"{round_s:.2f} s per full round"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by batch row with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from speculative_decoding_forward_amd import binding, rounds, synth
+
+    assert torch.cuda.is_available(), "no GPU"
+    wl = synth.WORKLOADS[args.workload]
+    B = args.batch or wl.batch
+    K = args.K or wl.K
+    knobs = (wl.temperature, wl.top_k, wl.top_p)
+    dev = "cuda"
+    torch.manual_seed(args.seed)
+    Wt = synth.make_weights(wl.target, seed=args.seed, model_id=synth.TARGET, device=dev)
+    Wd = synth.make_weights(wl.draft, seed=args.seed, model_id=synth.DRAFT, device=dev)
+    rounds_total = args.warmup + args.steps
+    max_len = wl.ctx + (rounds_total + 1) * (K + 1) + 2
+    dec = rounds.SpecDecoder(wl.target, Wt, wl.draft, Wd, B, K, max_len, knobs, seed=args.seed)
+    ctx = synth.context_ids(args.seed, B, wl.ctx, wl.target.vocab)
+    dec.prefill(ctx)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for r in range(args.warmup):
+        dec.step(r)
+    torch.cuda.synchronize()
+
+    binding.timing_enable(True)
+    binding.timing_read()
+    n_out_sum = torch.zeros(B, dtype=torch.int64, device=dev)
+    ev_v = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    len_start = dec.tkv.len.cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        r = args.warmup + i
+        dec.draft_phase(r)
+        ev_v[i][0].record(stream)
+        dec.verify_phase()
+        ev_v[i][1].record(stream)
+        dec.accept_phase(r)
+        n_out_sum += dec.n_out
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.timing_enable(False)
+    gemm_ms, gemm_n, attn_ms, attn_n = binding.timing_read()
+    wall = t1 - t0
+    tokens = int(n_out_sum.sum().item())
+    verify_ms = np.array([a.elapsed_time(b) for a, b in ev_v])
+
+    # bytes: GEMMs of the target verify (R = B*(K+1)) and of the draft steps
+    R_v = B * (K + 1)
+    gb_v, gn_v = gemm_bytes_per_verify(wl.target, R_v)
+    gb_d0, gn_d0 = gemm_bytes_per_verify(wl.draft, B * 2)
+    gb_d1, gn_d1 = gemm_bytes_per_verify(wl.draft, B)
+    gemm_bytes = args.steps * (gb_v + gb_d0 + (K - 1) * gb_d1)
+    assert gemm_n == args.steps * (gn_v + gn_d0 + (K - 1) * gn_d1), (gemm_n,)
+    gemm_avg_bytes = gemm_bytes / gemm_n
+    gemm_avg_s = gemm_ms / 1e3 / gemm_n
+    achieved = gemm_avg_bytes / gemm_avg_s / 1e9
+    # verify pass as a whole, at the mean cache length of the timed rounds
+    len_end = dec.tkv.len.cpu().numpy().astype(np.float64)
+    vb = verify_bytes(wl.target, B, K, (len_start + len_end) / 2)
+    v_med = float(np.median(verify_ms))
+    accepted = tokens - B * args.steps
+    alpha_hat = accepted / (B * args.steps * K)
+    res = {
+        "metric": "accepted tokens/s + verify-pass HBM GB/s (% of peak), 7B-shape bf16, K=5",
+        "value": tokens / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.target.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded random-init weights (N(0,0.02^2)), uniform context ids",
+        "config": {"workload": f"{args.workload}-shape speculative rounds",
+                   "target": f"L{wl.target.n_layers} d{wl.target.d_model} "
+                             f"F{wl.target.d_ffn} {wl.target.ffn_kind} V{wl.target.vocab}",
+                   "draft": f"L{wl.draft.n_layers} d{wl.draft.d_model} F{wl.draft.d_ffn}",
+                   "batch": B, "K": K, "context": wl.ctx, "temperature": wl.temperature,
+                   "top_p": wl.top_p, "parallelism": "1 GPU"},
+        "verify_ms_median": v_med,
+        "verify_ms_p10_p90": [float(np.percentile(verify_ms, 10)),
+                              float(np.percentile(verify_ms, 90))],
+        "verify_GBps": vb / (v_med / 1e3) / 1e9,
+        "verify_frac_of_peak": vb / (v_med / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "verify_bytes": vb,
+        "tokens_per_round_per_row": tokens / (B * args.steps),
+        "alpha_measured": alpha_hat,
+        "attention_ms_per_round": attn_ms / args.steps,
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_bf16 (weight-streaming GEMM)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": gemm_avg_bytes,
+                     "avg_launch_us": gemm_avg_s * 1e6, "launches": gemm_n},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, B, K, tokens / args.steps, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -170,6 +170,15 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
                             int32_t* x_tilde, float* q_logits, int32_t* row_status,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Verify-input assembly ([ZSM] "The algorithm": the target scores the context followed
+ * by the drafts; [CANON] listing, target call over ctx and xs): tokens[b] =
+ * [y_prev, x~_0 .. x~_{K-1}] with y_prev = pending[b, n_pending[b] - 1], the newest
+ * committed token, which the target cache does not hold yet.
+ *   pending [B, 2], n_pending [B] in {1, 2}, x_tilde [B, K]  ->  tokens [B, K+1] int32 */
+spec_status spec_verify_tokens(const int32_t* pending, const int32_t* n_pending,
+                               const int32_t* x_tilde, int B, int K, int32_t* tokens,
+                               void* stream);
+
 /* ------------------------------------------------------------------ the rule ------ */
 
 /* Workspace bytes for spec_accept_resample with B rows and K drafts. */
@@ -213,6 +222,18 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
                                  spec_kv* tkv, spec_kv* dkv, int32_t* pending,
                                  int32_t* n_pending, void* const* debug, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ measurement --- */
+
+/* Kernel timing for measurement.  While enabled, HIP events are recorded on the launch
+ * stream immediately before and after every weight-GEMM launch and every attention
+ * launch (split-KV kernel + merge) of spec_verify_forward / spec_draft_step.
+ * spec_timing_read waits for the recorded events, returns the summed elapsed times
+ * (ms) and launch counts since the last read, and clears them.  Events are created
+ * on first use and reused; timing adds the event records to the stream. */
+spec_status spec_timing_enable(int on);
+spec_status spec_timing_read(double* gemm_ms, int* gemm_launches, double* attn_ms,
+                             int* attn_launches);
 
 /* ------------------------------------------------------------------ misc ---------- */
 

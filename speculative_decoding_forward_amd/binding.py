@@ -23,8 +23,9 @@ SYMBOLS = [
     "spec_model_n_weights", "spec_model_create", "spec_model_destroy", "spec_kv_bytes",
     "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_rollback",
     "spec_workspace_bytes", "spec_verify_forward", "spec_draft_step",
-    "spec_accept_workspace_bytes", "spec_accept_resample", "spec_status_str",
-    "spec_last_hip_error", "spec_abi_version",
+    "spec_accept_workspace_bytes", "spec_accept_resample", "spec_verify_tokens",
+    "spec_status_str", "spec_last_hip_error", "spec_abi_version", "spec_timing_enable",
+    "spec_timing_read",
 ]
 
 
@@ -86,11 +87,15 @@ def load(path=None):
         "spec_verify_forward": (I32, [P, P, P, P, I32, I32, P, P, P, SZ, P]),
         "spec_draft_step": (I32, [P, P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, SZ, P]),
         "spec_accept_workspace_bytes": (SZ, [I32, I32]),
+        "spec_verify_tokens": (I32, [P, P, P, I32, I32, P, P]),
         "spec_accept_resample": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P,
                                        P, P, ctypes.POINTER(P), P, SZ, P]),
         "spec_status_str": (ctypes.c_char_p, [I32]),
         "spec_last_hip_error": (I32, []),
         "spec_abi_version": (I32, []),
+        "spec_timing_enable": (I32, [I32]),
+        "spec_timing_read": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32),
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -204,6 +209,12 @@ def draft_step(model: Model, kv: KVCache, in_tok, n_in, step, knobs, seed, rnd, 
            "spec_draft_step")
 
 
+def verify_tokens(pending, n_pending, x_tilde, tokens, stream=None):
+    B, K = x_tilde.shape
+    _check(load().spec_verify_tokens(_ptr(pending), _ptr(n_pending), _ptr(x_tilde), B, K,
+                                     _ptr(tokens), _stream(stream)), "spec_verify_tokens")
+
+
 def accept_workspace(B, K, device="cuda"):
     return _alloc(load().spec_accept_workspace_bytes(B, K), device)
 
@@ -226,3 +237,16 @@ def accept_resample(p_logits, q_logits, x_tilde, knobs, seed, rnd, out_tok, n_ou
         _ptr(out_tok), _ptr(n_out), _ptr(row_status), tkv.handle if tkv else None,
         dkv.handle if dkv else None, _ptr(pending), _ptr(n_pending), dbg, _ptr(ws), ws.numel(),
         _stream(stream)), "spec_accept_resample")
+
+
+def timing_enable(on=True):
+    _check(load().spec_timing_enable(1 if on else 0), "spec_timing_enable")
+
+
+def timing_read():
+    """(gemm_ms, gemm_launches, attn_ms, attn_launches) since the last read."""
+    gm, am = ctypes.c_double(), ctypes.c_double()
+    gn, an = I32(), I32()
+    _check(load().spec_timing_read(ctypes.byref(gm), ctypes.byref(gn), ctypes.byref(am),
+                                   ctypes.byref(an)), "spec_timing_read")
+    return gm.value, gn.value, am.value, an.value

@@ -8,7 +8,10 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <utility>
+#include <vector>
 
 #include "internal.h"
 
@@ -131,6 +134,45 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   return w;
 }
 
+// Kernel timing (measurement only): pairs of events around GEMM / attention launches.
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<int, int>> gemm, attn;  // indices into pool (start, stop)
+  size_t used = 0;
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Timing g_timing;
+std::mutex g_timing_mu;
+
+struct TimedLaunch {
+  std::vector<std::pair<int, int>>* list = nullptr;
+  int start = -1;
+  hipStream_t s;
+  TimedLaunch(std::vector<std::pair<int, int>>& l, hipStream_t st) : s(st) {
+    if (!g_timing.on) return;
+    hipEvent_t e = g_timing.next();
+    if (!e) return;
+    list = &l;
+    start = (int)g_timing.used - 1;
+    hipEventRecord(e, s);
+  }
+  ~TimedLaunch() {
+    if (!list) return;
+    hipEvent_t e = g_timing.next();
+    if (!e) return;
+    hipEventRecord(e, s);
+    list->push_back({start, (int)g_timing.used - 1});
+  }
+};
+
 // The forward pass shared by the verify call, draft steps and prefill chunks.
 spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
                     const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
@@ -150,23 +192,41 @@ spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
     char* kl = (char*)kv->data + (size_t)l * kv->layer_stride * e;
     char* vl = kl + kv->kv_stride * e;
     SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm1, R, d, c.norm_eps, dt, w.h, s));
-    SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.wqkv, nullptr, R, 3 * d, 3 * d, d, w.y, 0, nullptr, 0, s));
+    {
+      TimedLaunch t(g_timing.gemm, s);
+      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.wqkv, nullptr, R, 3 * d, 3 * d, d, w.y, 0, nullptr, 0, s));
+    }
     SPEC_LAUNCH(launch_rope_append(dt, w.y, B, M, H, hd, c.rope_theta, w.pos0, w.ntok_eff, w.q,
                                    kl, vl, kv->row_stride, kv->head_stride, kv->max_len, s));
-    SPEC_LAUNCH(launch_attention(dt, w.q, kl, vl, kv->row_stride, kv->head_stride, B, M, H, hd,
-                                 w.pos0, w.ntok_eff, w.part, nsplit, kv->max_len, w.att, s));
-    SPEC_LAUNCH(launch_gemm_ex(dt, w.att, L.wo, nullptr, R, d, d, d, w.x, 1, nullptr, 0, s));
+    {
+      TimedLaunch t(g_timing.attn, s);
+      SPEC_LAUNCH(launch_attention(dt, w.q, kl, vl, kv->row_stride, kv->head_stride, B, M, H, hd,
+                                   w.pos0, w.ntok_eff, w.part, nsplit, kv->max_len, w.att, s));
+    }
+    {
+      TimedLaunch t(g_timing.gemm, s);
+      SPEC_LAUNCH(launch_gemm_ex(dt, w.att, L.wo, nullptr, R, d, d, d, w.x, 1, nullptr, 0, s));
+    }
     SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm2, R, d, c.norm_eps, dt, w.h, s));
-    if (swiglu) {
-      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, L.w_up2, R, 2 * F, F, d, w.y, 0, nullptr, 0, s));
-    } else {
-      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, nullptr, R, F, F, d, w.y, 0, nullptr, 0, s));
+    {
+      TimedLaunch t(g_timing.gemm, s);
+      if (swiglu) {
+        SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, L.w_up2, R, 2 * F, F, d, w.y, 0, nullptr, 0, s));
+      } else {
+        SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, nullptr, R, F, F, d, w.y, 0, nullptr, 0, s));
+      }
     }
     SPEC_LAUNCH(launch_act(dt, c.ffn_kind, w.y, R, F, w.a, s));
-    SPEC_LAUNCH(launch_gemm_ex(dt, w.a, L.w_down, nullptr, R, d, d, F, w.x, 1, nullptr, 0, s));
+    {
+      TimedLaunch t(g_timing.gemm, s);
+      SPEC_LAUNCH(launch_gemm_ex(dt, w.a, L.w_down, nullptr, R, d, d, F, w.x, 1, nullptr, 0, s));
+    }
   }
   SPEC_LAUNCH(launch_rmsnorm(w.x, m->norm_f, R, d, c.norm_eps, dt, w.h, s));
-  SPEC_LAUNCH(launch_gemm_ex(dt, w.h, m->head, nullptr, R, V, V, d, logits, 0, w.ntok_eff, M, s));
+  {
+    TimedLaunch t(g_timing.gemm, s);
+    SPEC_LAUNCH(launch_gemm_ex(dt, w.h, m->head, nullptr, R, V, V, d, logits, 0, w.ntok_eff, M, s));
+  }
   return SPEC_OK;
 }
 
@@ -335,6 +395,15 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
   return SPEC_OK;
 }
 
+spec_status spec_verify_tokens(const int32_t* pending, const int32_t* n_pending,
+                               const int32_t* x_tilde, int B, int K, int32_t* tokens,
+                               void* stream) {
+  if (!pending || !n_pending || !x_tilde || !tokens || B < 1 || K < 1) return SPEC_E_INVALID;
+  SPEC_LAUNCH(launch_verify_tokens(pending, n_pending, x_tilde, B, K, tokens,
+                                   (hipStream_t)stream));
+  return SPEC_OK;
+}
+
 size_t spec_accept_workspace_bytes(int B, int K) {
   if (B < 1 || K < 1) return 0;
   return align_up((size_t)B * K * 4) + 2 * align_up((size_t)B * (K + 1) * 4);
@@ -376,6 +445,38 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
   if (debug && debug[3])
     SPEC_LAUNCH(hipMemcpyAsync(debug[3], res_cand, (size_t)B * (K + 1) * 4,
                                hipMemcpyDeviceToDevice, s));
+  return SPEC_OK;
+}
+
+spec_status spec_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing.on = on != 0;
+  return SPEC_OK;
+}
+
+spec_status spec_timing_read(double* gemm_ms, int* gemm_launches, double* attn_ms,
+                             int* attn_launches) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  auto total = [](const std::vector<std::pair<int, int>>& l, double* ms, int* n) -> hipError_t {
+    double t = 0.0;
+    for (auto& pr : l) {
+      hipError_t e = hipEventSynchronize(g_timing.pool[pr.second]);
+      if (e != hipSuccess) return e;
+      float x = 0.f;
+      e = hipEventElapsedTime(&x, g_timing.pool[pr.first], g_timing.pool[pr.second]);
+      if (e != hipSuccess) return e;
+      t += x;
+    }
+    if (ms) *ms = t;
+    if (n) *n = (int)l.size();
+    return hipSuccess;
+  };
+  hipError_t e = total(g_timing.gemm, gemm_ms, gemm_launches);
+  if (e == hipSuccess) e = total(g_timing.attn, attn_ms, attn_launches);
+  g_timing.gemm.clear();
+  g_timing.attn.clear();
+  g_timing.used = 0;
+  if (e != hipSuccess) return hip_fail(e);
   return SPEC_OK;
 }
 

@@ -89,5 +89,8 @@ hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
                                const int32_t* x_tilde, int B, int K, int step,
                                int32_t* tokens, int32_t* n_tok, hipStream_t s);
 hipError_t launch_rollback(int32_t* len, const int32_t* new_len, int B, hipStream_t s);
+hipError_t launch_verify_tokens(const int32_t* pending, const int32_t* n_pending,
+                                const int32_t* x_tilde, int B, int K, int32_t* tokens,
+                                hipStream_t s);
 
 }  // namespace specdec

@@ -458,6 +458,18 @@ __global__ void k_draft_tokens(const int32_t* __restrict__ in_tok, const int32_t
   }
 }
 
+// tokens[b] = [pending[b, n_pending[b] - 1], x~_0 .. x~_{K-1}]
+__global__ void k_verify_tokens(const int32_t* __restrict__ pending,
+                                const int32_t* __restrict__ n_pending,
+                                const int32_t* __restrict__ x_tilde, int B, int K,
+                                int32_t* __restrict__ tokens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int np = min(max(n_pending[b], 1), 2);
+  tokens[(size_t)b * (K + 1)] = pending[2 * b + np - 1];
+  for (int j = 0; j < K; ++j) tokens[(size_t)b * (K + 1) + 1 + j] = x_tilde[b * K + j];
+}
+
 __global__ void k_rollback(int32_t* __restrict__ len, const int32_t* __restrict__ new_len, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) len[b] = min(len[b], max(new_len[b], 0));
@@ -510,6 +522,13 @@ hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
                                const int32_t* x_tilde, int B, int K, int step,
                                int32_t* tokens, int32_t* n_tok, hipStream_t s) {
   k_draft_tokens<<<cdiv(B, 64), 64, 0, s>>>(in_tok, n_in, x_tilde, B, K, step, tokens, n_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_tokens(const int32_t* pending, const int32_t* n_pending,
+                                const int32_t* x_tilde, int B, int K, int32_t* tokens,
+                                hipStream_t s) {
+  k_verify_tokens<<<cdiv(B, 64), 64, 0, s>>>(pending, n_pending, x_tilde, B, K, tokens);
   return hipGetLastError();
 }
 
