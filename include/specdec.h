@@ -163,12 +163,15 @@ spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t*
  * in {1,2}: the draft's pending tokens); step s > 0 takes x_tilde[b, s-1].
  *   x_tilde  [B, K] int32, column `step` written
  *   q_logits [B, K, V] fp32, row `step` written (the draft logits at the last input)
- * A step-0 call records the row's pre-round cache length for spec_accept_resample. */
+ * A step-0 call records the row's pre-round cache length for spec_accept_resample.
+ * round_dev (device, NULL = use `round`): when set, the round number is read from
+ * *round_dev at execution time, so a captured HIP graph of a whole round can be
+ * replayed round after round (spec_accept_resample advances the counter). */
 spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t* in_tok,
                             const int32_t* n_in, int B, int K, int step,
                             const spec_sampling* knobs, uint64_t seed, uint64_t round,
-                            int32_t* x_tilde, float* q_logits, int32_t* row_status,
-                            void* ws, size_t ws_bytes, void* stream);
+                            const uint64_t* round_dev, int32_t* x_tilde, float* q_logits,
+                            int32_t* row_status, void* ws, size_t ws_bytes, void* stream);
 
 /* Verify-input assembly ([ZSM] "The algorithm": the target scores the context followed
  * by the drafts; [CANON] listing, target call over ctx and xs): tokens[b] =
@@ -207,6 +210,8 @@ size_t spec_accept_workspace_bytes(int B, int K);
  *        if a = K
  *   pending [B, 2] / n_pending [B]: the draft's pending tokens for the next round:
  *        [y] if a < K, [x~_{K-1}, y] if a = K
+ * round_dev (device, NULL = use `round`): when set, the round number is read from
+ *   *round_dev and *round_dev is incremented by one after the rows are decided.
  * A row with NONFINITE, BAD_TOKEN or KV_OVERFLOW emits nothing (n_out = 0) and its
  * caches are restored to their pre-round lengths.
  * V <= 32768 (else SPEC_E_UNSUPPORTED); 1 <= K <= 16.
@@ -218,7 +223,8 @@ size_t spec_accept_workspace_bytes(int B, int K);
 spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
                                  const int32_t* x_tilde, int B, int K, int V,
                                  const spec_sampling* knobs, uint64_t seed, uint64_t round,
-                                 int32_t* out_tok, int32_t* n_out, int32_t* row_status,
+                                 uint64_t* round_dev, int32_t* out_tok, int32_t* n_out,
+                                 int32_t* row_status,
                                  spec_kv* tkv, spec_kv* dkv, int32_t* pending,
                                  int32_t* n_pending, void* const* debug, void* ws,
                                  size_t ws_bytes, void* stream);

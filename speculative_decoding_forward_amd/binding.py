@@ -85,10 +85,11 @@ def load(path=None):
         "spec_kv_rollback": (I32, [P, P, P]),
         "spec_workspace_bytes": (SZ, [cfgp, I32, I32, I32]),
         "spec_verify_forward": (I32, [P, P, P, P, I32, I32, P, P, P, SZ, P]),
-        "spec_draft_step": (I32, [P, P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, SZ, P]),
+        "spec_draft_step": (I32, [P, P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P, SZ,
+                                  P]),
         "spec_accept_workspace_bytes": (SZ, [I32, I32]),
         "spec_verify_tokens": (I32, [P, P, P, I32, I32, P, P]),
-        "spec_accept_resample": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P,
+        "spec_accept_resample": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P, P,
                                        P, P, ctypes.POINTER(P), P, SZ, P]),
         "spec_status_str": (ctypes.c_char_p, [I32]),
         "spec_last_hip_error": (I32, []),
@@ -200,13 +201,14 @@ def verify_forward(model: Model, kv: KVCache, tokens, logits, ws, n_tok=None, ro
 
 
 def draft_step(model: Model, kv: KVCache, in_tok, n_in, step, knobs, seed, rnd, x_tilde,
-               q_logits, ws, row_status=None, stream=None):
+               q_logits, ws, row_status=None, stream=None, round_dev=None):
+    """round_dev: optional int64 device scalar holding the round number (graph replay)."""
     B, K = x_tilde.shape
     smp = Sampling(*knobs)
     _check(load().spec_draft_step(model.handle, kv.handle, _ptr(in_tok), _ptr(n_in), B, K, step,
-                                  ctypes.byref(smp), seed, rnd, _ptr(x_tilde), _ptr(q_logits),
-                                  _ptr(row_status), _ptr(ws), ws.numel(), _stream(stream)),
-           "spec_draft_step")
+                                  ctypes.byref(smp), seed, rnd, _ptr(round_dev), _ptr(x_tilde),
+                                  _ptr(q_logits), _ptr(row_status), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "spec_draft_step")
 
 
 def verify_tokens(pending, n_pending, x_tilde, tokens, stream=None):
@@ -221,7 +223,7 @@ def accept_workspace(B, K, device="cuda"):
 
 def accept_resample(p_logits, q_logits, x_tilde, knobs, seed, rnd, out_tok, n_out, row_status,
                     ws, tkv=None, dkv=None, pending=None, n_pending=None, debug=None,
-                    stream=None):
+                    stream=None, round_dev=None):
     """p_logits [B, K+1, V], q_logits [B, K, V] fp32; x_tilde [B, K] int32.
 
     debug: optional (p_probs, q_probs, accept, cand) tensors or None entries.
@@ -234,7 +236,8 @@ def accept_resample(p_logits, q_logits, x_tilde, knobs, seed, rnd, out_tok, n_ou
         dbg = (P * 4)(*[(t.data_ptr() if t is not None else None) for t in debug])
     _check(load().spec_accept_resample(
         _ptr(p_logits), _ptr(q_logits), _ptr(x_tilde), B, K, V, ctypes.byref(smp), seed, rnd,
-        _ptr(out_tok), _ptr(n_out), _ptr(row_status), tkv.handle if tkv else None,
+        _ptr(round_dev), _ptr(out_tok), _ptr(n_out), _ptr(row_status),
+        tkv.handle if tkv else None,
         dkv.handle if dkv else None, _ptr(pending), _ptr(n_pending), dbg, _ptr(ws), ws.numel(),
         _stream(stream)), "spec_accept_resample")
 

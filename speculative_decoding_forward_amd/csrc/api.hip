@@ -91,16 +91,19 @@ struct FwdWS {
   int32_t* pos0;
   int32_t* ntok_eff;
   int32_t* tok_eff;
-  int32_t* tok2;    // draft-step input tokens [B, 2]
-  int32_t* ntok2;   // draft-step counts [B]
-  float* x;         // residual stream [R, d]
-  void* h;          // normed activations [R, d]
-  void* a;          // FFN activations [R, F]
-  float* y;         // GEMM outputs [R, max(3d, 2F)]
-  void* q;          // rotated queries [R, d]
-  void* att;        // attention output [R, d]
-  float* part;      // attention partials
-  float* logits;    // draft-step logits [R, V]
+  int32_t* tok2;      // draft-step input tokens [B, 2]
+  int32_t* ntok2;     // draft-step counts [B]
+  unsigned* counters; // completion counters: [B*H] attention + 1 GEMM
+  int n_counters;
+  float* x;           // residual stream [R, d] fp32
+  void* h;            // normed activations [R, d]
+  void* a;            // FFN activations [R, F]
+  float* y;           // fp32 models: GEMM outputs [R, max(3d, 2F)]
+  void* q;            // rotated queries [R, d]
+  void* att;          // attention output [R, d]
+  float* part;        // attention partials
+  double* ss_part;    // residual GEMM: per-workgroup row sums of squares [d/16, R]
+  float* logits;      // draft-step logits [R, V]
   size_t total;
 };
 
@@ -110,7 +113,7 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   const size_t e = elt_bytes(c);
   const size_t d = c.d_model, F = c.d_ffn, V = c.vocab;
   const size_t ffn_out = c.ffn_kind == SPEC_FFN_SWIGLU ? 2 * F : F;
-  const size_t nsplit = (size_t)cdiv(max_len, attn_chunk());
+  const size_t nsplit = (size_t)cdiv(max_len, attn_split());
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -122,69 +125,67 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.tok_eff = (int32_t*)take(R * 4);
   w.tok2 = (int32_t*)take((size_t)B * 2 * 4);
   w.ntok2 = (int32_t*)take(B * 4);
+  // attention completion counters [B*H*ceil(M/8)] followed by 64 zero words; prep
+  // clears all of them at the start of every forward
+  w.n_counters = B * c.n_heads * cdiv(M, 8) + 64;
+  w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
   w.h = take(R * d * e);
   w.a = take(R * F * e);
-  w.y = (float*)take(R * std::max(3 * d, ffn_out) * 4);
+  w.y = (float*)take(c.dtype == SPEC_DT_F32 ? R * std::max(3 * d, ffn_out) * 4 : 0);
   w.q = take(R * d * e);
   w.att = take(R * d * e);
-  w.part = (float*)take((size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4);
+  w.part = (float*)take(c.dtype == SPEC_DT_BF16
+                            ? (size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4
+                            : 0);
   w.logits = (float*)take(R * V * 4);
+  w.ss_part = (double*)take(c.dtype == SPEC_DT_BF16 ? (d / 16) * R * 8 : 0);
   w.total = off;
   return w;
 }
 
-// Kernel timing (measurement only): pairs of events around GEMM / attention launches.
+// Kernel timing (measurement only): start/stop events attached to the dispatch packets
+// of GEMM and attention launches (hipExtLaunchKernelGGL), so no extra commands are
+// queued between kernels.
 struct Timing {
   bool on = false;
   std::vector<hipEvent_t> pool;
   std::vector<std::pair<int, int>> gemm, attn;  // indices into pool (start, stop)
   size_t used = 0;
-  hipEvent_t next() {
+  int next() {
     if (used == pool.size()) {
       hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return -1;
       pool.push_back(e);
     }
-    return pool[used++];
+    return (int)used++;
   }
 };
 Timing g_timing;
 std::mutex g_timing_mu;
 
-struct TimedLaunch {
-  std::vector<std::pair<int, int>>* list = nullptr;
-  int start = -1;
-  hipStream_t s;
-  TimedLaunch(std::vector<std::pair<int, int>>& l, hipStream_t st) : s(st) {
-    if (!g_timing.on) return;
-    hipEvent_t e = g_timing.next();
-    if (!e) return;
-    list = &l;
-    start = (int)g_timing.used - 1;
-    hipEventRecord(e, s);
-  }
-  ~TimedLaunch() {
-    if (!list) return;
-    hipEvent_t e = g_timing.next();
-    if (!e) return;
-    hipEventRecord(e, s);
-    list->push_back({start, (int)g_timing.used - 1});
-  }
+struct Ev {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
 };
 
-// The forward pass shared by the verify call, draft steps and prefill chunks.
-spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
-                    const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
-                    int record_base, const FwdWS& w, hipStream_t s) {
+Ev timed(std::vector<std::pair<int, int>>& list) {
+  Ev ev;
+  if (!g_timing.on) return ev;
+  const int a = g_timing.next(), b = g_timing.next();
+  if (a < 0 || b < 0) return ev;
+  list.push_back({a, b});
+  ev.e0 = g_timing.pool[a];
+  ev.e1 = g_timing.pool[b];
+  return ev;
+}
+
+spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
+                        const FwdWS& w, hipStream_t s) {
   const spec_model_cfg& c = m->cfg;
   const int dt = c.dtype;
   const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
-  const int nsplit = cdiv(kv->max_len, attn_chunk());
-  SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, V, kv->len, kv->base, record_base, kv->max_len,
-                          w.pos0, w.ntok_eff, w.tok_eff, row_status, s));
   SPEC_LAUNCH(launch_embed(m->embed, dt, w.tok_eff, R, d, w.x, s));
   const int swiglu = c.ffn_kind == SPEC_FFN_SWIGLU;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -192,42 +193,165 @@ spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
     char* kl = (char*)kv->data + (size_t)l * kv->layer_stride * e;
     char* vl = kl + kv->kv_stride * e;
     SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm1, R, d, c.norm_eps, dt, w.h, s));
-    {
-      TimedLaunch t(g_timing.gemm, s);
-      SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.wqkv, nullptr, R, 3 * d, 3 * d, d, w.y, 0, nullptr, 0, s));
-    }
+    Ev e1 = timed(g_timing.gemm);
+    SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.wqkv, nullptr, 3 * d, R,
+                                3 * d, d, w.y, 0, nullptr, M, s, e1.e0, e1.e1));
     SPEC_LAUNCH(launch_rope_append(dt, w.y, B, M, H, hd, c.rope_theta, w.pos0, w.ntok_eff, w.q,
                                    kl, vl, kv->row_stride, kv->head_stride, kv->max_len, s));
-    {
-      TimedLaunch t(g_timing.attn, s);
-      SPEC_LAUNCH(launch_attention(dt, w.q, kl, vl, kv->row_stride, kv->head_stride, B, M, H, hd,
-                                   w.pos0, w.ntok_eff, w.part, nsplit, kv->max_len, w.att, s));
-    }
-    {
-      TimedLaunch t(g_timing.gemm, s);
-      SPEC_LAUNCH(launch_gemm_ex(dt, w.att, L.wo, nullptr, R, d, d, d, w.x, 1, nullptr, 0, s));
-    }
+    Ev e2 = timed(g_timing.attn);
+    SPEC_LAUNCH(launch_attention_f32((const float*)w.q, (const float*)kl, (const float*)vl,
+                                     kv->row_stride, kv->head_stride, B, M, H, hd, w.pos0,
+                                     w.ntok_eff, kv->max_len, (float*)w.att, s, e2.e0, e2.e1));
+    Ev e3 = timed(g_timing.gemm);
+    SPEC_LAUNCH(launch_gemm_f32((const float*)w.att, (const float*)L.wo, nullptr, d, R, d, d,
+                                w.x, 1, nullptr, M, s, e3.e0, e3.e1));
     SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm2, R, d, c.norm_eps, dt, w.h, s));
-    {
-      TimedLaunch t(g_timing.gemm, s);
-      if (swiglu) {
-        SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, L.w_up2, R, 2 * F, F, d, w.y, 0, nullptr, 0, s));
-      } else {
-        SPEC_LAUNCH(launch_gemm_ex(dt, w.h, L.w_up, nullptr, R, F, F, d, w.y, 0, nullptr, 0, s));
-      }
-    }
+    Ev e4 = timed(g_timing.gemm);
+    if (swiglu)
+      SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.w_up,
+                                  (const float*)L.w_up2, F, R, 2 * F, d, w.y, 0, nullptr, M, s,
+                                  e4.e0, e4.e1));
+    else
+      SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.w_up, nullptr, F, R, F, d,
+                                  w.y, 0, nullptr, M, s, e4.e0, e4.e1));
     SPEC_LAUNCH(launch_act(dt, c.ffn_kind, w.y, R, F, w.a, s));
-    {
-      TimedLaunch t(g_timing.gemm, s);
-      SPEC_LAUNCH(launch_gemm_ex(dt, w.a, L.w_down, nullptr, R, d, d, F, w.x, 1, nullptr, 0, s));
-    }
+    Ev e5 = timed(g_timing.gemm);
+    SPEC_LAUNCH(launch_gemm_f32((const float*)w.a, (const float*)L.w_down, nullptr, d, R, d, F,
+                                w.x, 1, nullptr, M, s, e5.e0, e5.e1));
   }
   SPEC_LAUNCH(launch_rmsnorm(w.x, m->norm_f, R, d, c.norm_eps, dt, w.h, s));
-  {
-    TimedLaunch t(g_timing.gemm, s);
-    SPEC_LAUNCH(launch_gemm_ex(dt, w.h, m->head, nullptr, R, V, V, d, logits, 0, w.ntok_eff, M, s));
-  }
+  Ev e6 = timed(g_timing.gemm);
+  SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)m->head, nullptr, V, R, V, d,
+                              logits, 0, w.ntok_eff, M, s, e6.e0, e6.e1));
   return SPEC_OK;
+}
+
+// bf16 models: 7 kernels per layer.
+//   QKV GEMM (+ RoPE, q out, K/V append) -> attention (+ split merge) ->
+//   O GEMM (+ residual, row sums of squares) -> row norm -> up GEMM (+ SwiGLU / GELU)
+//   -> down GEMM (+ residual, row sums of squares) -> row norm (next layer's / final)
+spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
+                         const FwdWS& w, hipStream_t s) {
+  const spec_model_cfg& c = m->cfg;
+  const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
+            hd = c.head_dim;
+  const size_t e = elt_bytes(c);
+  unsigned* attn_counters = w.counters;
+  SPEC_LAUNCH(launch_embed_norm(m->embed, c.dtype, w.tok_eff, R, d, m->layers[0].norm1,
+                                c.norm_eps, w.x, w.h, s));
+  GemmArgs base{};
+  base.R = R;
+  base.M = M;
+  base.ntok_eff = w.ntok_eff;
+  base.pos0 = w.pos0;
+  base.d = d;
+  base.hd = hd;
+  base.theta = c.rope_theta;
+  base.row_stride = kv->row_stride;
+  base.head_stride = kv->head_stride;
+  base.max_len = kv->max_len;
+  base.ss_part = w.ss_part;
+  base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const spec_model::Layer& L = m->layers[l];
+    uint16_t* kl = (uint16_t*)((char*)kv->data + (size_t)l * kv->layer_stride * e);
+    uint16_t* vl = kl + kv->kv_stride;
+    {
+      GemmArgs g = base;
+      g.mode = EPI_QKV_ROPE;
+      g.A = (const uint16_t*)w.h;
+      g.lda = d;
+      g.W = g.W2 = (const uint16_t*)L.wqkv;
+      g.N = g.N1 = 3 * d;
+      g.K = d;
+      g.q_out = (uint16_t*)w.q;
+      g.kc = kl;
+      g.vc = vl;
+      Ev ev = timed(g_timing.gemm);
+      SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
+    }
+    {
+      Ev ev = timed(g_timing.attn);
+      SPEC_LAUNCH(launch_attention_bf16((const uint16_t*)w.q, kl, vl, kv->row_stride,
+                                        kv->head_stride, B, M, H, hd, w.pos0, w.ntok_eff,
+                                        w.part, attn_counters, kv->max_len,
+                                        (uint16_t*)w.att, s, ev.e0, ev.e1));
+    }
+    {
+      GemmArgs g = base;
+      g.mode = EPI_RESID;
+      g.A = (const uint16_t*)w.att;
+      g.lda = d;
+      g.W = g.W2 = (const uint16_t*)L.wo;
+      g.N = g.N1 = d;
+      g.K = d;
+      g.C = w.x;
+      g.ldc = d;
+      Ev ev = timed(g_timing.gemm);
+      SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
+      SPEC_LAUNCH(launch_rownorm(w.x, w.ss_part, d / 16, R, d, L.norm2, c.norm_eps,
+                                 (uint16_t*)w.h, s));
+    }
+    {
+      GemmArgs g = base;
+      g.A = (const uint16_t*)w.h;
+      g.lda = d;
+      g.K = d;
+      g.act_out = (uint16_t*)w.a;
+      g.W = (const uint16_t*)L.w_up;
+      if (c.ffn_kind == SPEC_FFN_SWIGLU) {
+        g.mode = EPI_SWIGLU;
+        g.W2 = (const uint16_t*)L.w_up2;
+        g.N1 = F;
+        g.N = 2 * F;
+      } else {
+        g.mode = EPI_GELU;
+        g.W2 = g.W;
+        g.N = g.N1 = F;
+      }
+      Ev ev = timed(g_timing.gemm);
+      SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
+    }
+    {
+      GemmArgs g = base;
+      g.mode = EPI_RESID;
+      g.A = (const uint16_t*)w.a;
+      g.lda = F;
+      g.W = g.W2 = (const uint16_t*)L.w_down;
+      g.N = g.N1 = d;
+      g.K = F;
+      g.C = w.x;
+      g.ldc = d;
+      Ev ev = timed(g_timing.gemm);
+      SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
+      SPEC_LAUNCH(launch_rownorm(w.x, w.ss_part, d / 16, R, d,
+                                 l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f,
+                                 c.norm_eps, (uint16_t*)w.h, s));
+    }
+  }
+  GemmArgs g = base;
+  g.mode = EPI_STORE;
+  g.A = (const uint16_t*)w.h;
+  g.lda = d;
+  g.W = g.W2 = (const uint16_t*)m->head;
+  g.N = g.N1 = V;
+  g.K = d;
+  g.C = logits;
+  g.ldc = V;
+  Ev ev = timed(g_timing.gemm);
+  SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
+  return SPEC_OK;
+}
+
+// The forward pass shared by the verify call, draft steps and prefill chunks.
+spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                    const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
+                    int record_base, const FwdWS& w, hipStream_t s) {
+  SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, m->cfg.vocab, kv->len, kv->base, record_base,
+                          kv->max_len, w.pos0, w.ntok_eff, w.tok_eff, row_status, w.counters,
+                          w.n_counters, s));
+  if (m->cfg.dtype == SPEC_DT_BF16) return forward_bf16(m, kv, B, M, logits, w, s);
+  return forward_f32(m, kv, B, M, logits, w, s);
 }
 
 bool kv_matches(const spec_model* m, const spec_kv* kv) {
@@ -371,8 +495,8 @@ spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t*
 spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t* in_tok,
                             const int32_t* n_in, int B, int K, int step,
                             const spec_sampling* knobs, uint64_t seed, uint64_t round,
-                            int32_t* x_tilde, float* q_logits, int32_t* row_status, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            const uint64_t* round_dev, int32_t* x_tilde, float* q_logits,
+                            int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
   if (!draft || !dkv || !x_tilde || !q_logits || !ws || !knobs_valid(knobs))
     return SPEC_E_INVALID;
   if (B < 1 || B > dkv->batch || K < 1 || K > 16 || step < 0 || step >= K)
@@ -391,7 +515,8 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
       forward(draft, dkv, w.tok2, w.ntok2, B, M, w.logits, row_status, step == 0 ? 1 : 0, w, s);
   if (st != SPEC_OK) return st;
   SPEC_LAUNCH(launch_draft_sample(w.logits, B, M, w.ntok2, step, K, draft->cfg.vocab,
-                                  to_knobs(knobs), seed, round, x_tilde, q_logits, s));
+                                  to_knobs(knobs), seed, round, round_dev, x_tilde, q_logits,
+                                  s));
   return SPEC_OK;
 }
 
@@ -412,7 +537,8 @@ size_t spec_accept_workspace_bytes(int B, int K) {
 spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
                                  const int32_t* x_tilde, int B, int K, int V,
                                  const spec_sampling* knobs, uint64_t seed, uint64_t round,
-                                 int32_t* out_tok, int32_t* n_out, int32_t* row_status,
+                                 uint64_t* round_dev, int32_t* out_tok, int32_t* n_out,
+                                 int32_t* row_status,
                                  spec_kv* tkv, spec_kv* dkv, int32_t* pending,
                                  int32_t* n_pending, void* const* debug, void* ws,
                                  size_t ws_bytes, void* stream) {
@@ -435,11 +561,12 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
   float* dbg_q = debug ? (float*)debug[1] : nullptr;
   hipStream_t s = (hipStream_t)stream;
   SPEC_LAUNCH(launch_accept_rows(p_logits, q_logits, x_tilde, B, K, V, to_knobs(knobs), seed,
-                                 round, res_acc, res_cand, res_status, dbg_p, dbg_q, s));
+                                 round, round_dev, res_acc, res_cand, res_status, dbg_p, dbg_q,
+                                 s));
   SPEC_LAUNCH(launch_select(x_tilde, B, K, res_acc, res_cand, res_status, out_tok, n_out,
                             row_status, tkv ? tkv->len : nullptr, tkv ? tkv->base : nullptr,
                             dkv ? dkv->len : nullptr, dkv ? dkv->base : nullptr, pending,
-                            n_pending, s));
+                            n_pending, round_dev, s));
   if (debug && debug[2])
     SPEC_LAUNCH(hipMemcpyAsync(debug[2], res_acc, (size_t)B * K * 4, hipMemcpyDeviceToDevice, s));
   if (debug && debug[3])

@@ -43,48 +43,89 @@ struct SamplingKnobs {
 // kernel launchers (defined in the .hip files)
 namespace specdec {
 
+// fused bf16 GEMM epilogues
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_GELU = 4 };
+
+struct GemmArgs {
+  const uint16_t* A;  // [R, K] bf16 activations
+  int lda;
+  const uint16_t* W;   // [N1, K] (rows < N1)
+  const uint16_t* W2;  // rows >= N1 (SwiGLU up matrix), else == W
+  int N1;
+  int R, N, K, mode;
+  float* C;  // STORE: logits; RESID: residual stream x
+  int ldc;
+  const int32_t* ntok_eff;  // [B] tokens per sequence (rows past it are padding)
+  int M;                    // rows per sequence
+  // QKV_ROPE
+  const int32_t* pos0;
+  int d, hd;
+  float theta;
+  uint16_t* q_out;
+  uint16_t* kc;
+  uint16_t* vc;
+  size_t row_stride, head_stride;
+  int max_len;
+  // SWIGLU / GELU
+  uint16_t* act_out;
+  // RESID
+  double* ss_part;        // [N/16, R] per-workgroup sums of squares
+  const uint16_t* zeros;  // >= 16 zero bytes (device)
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_rownorm(const float* x, const double* ss_part, int nparts, int R, int d,
+                          const float* gain, float eps, uint16_t* h, hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
+                           int N, int K, float* C, int accumulate, const int32_t* ntok_eff,
+                           int M, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_embed_norm(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
+                             const float* g, float eps, float* x, void* h, hipStream_t s);
+hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                 size_t row_stride, size_t head_stride, int B, int M, int H,
+                                 int hd, const int32_t* pos0, const int32_t* ntok_eff,
+                                 float* part, unsigned* counters, int max_len, uint16_t* out,
+                                 hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+int attn_split();  // cache positions per attention workgroup
+
 // forward pieces
 hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,
                        int32_t* len, int32_t* base, int record_base, int max_len,
                        int32_t* pos0, int32_t* ntok_eff, int32_t* tok_eff,
-                       int32_t* row_status, hipStream_t s);
+                       int32_t* row_status, unsigned* counters, int n_counters,
+                       hipStream_t s);
 hipError_t launch_embed(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
                         float* x, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const float* g, int R, int d, float eps,
                           int dtype, void* h, hipStream_t s);
-// C[R, N] (+)= A[R, K] W[N, K]^T; rows n >= N1 come from W2 (row n - N1); rows r with
-// r % rows_per_seq >= ntok_eff[r / rows_per_seq] are stored as 0 when ntok_eff is set.
-hipError_t launch_gemm_ex(int dtype, const void* A, const void* W, const void* W2, int R,
-                          int N, int N1, int K, float* C, int accumulate,
-                          const int32_t* ntok_eff, int rows_per_seq, hipStream_t s);
 hipError_t launch_rope_append(int dtype, const float* qkv, int B, int M, int H, int hd,
                               float theta, const int32_t* pos0, const int32_t* ntok_eff,
                               void* q_out, void* kcache, void* vcache, size_t row_stride,
                               size_t head_stride, int max_len, hipStream_t s);
-hipError_t launch_attention(int dtype, const void* q, const void* kcache, const void* vcache,
-                            size_t row_stride, size_t head_stride, int B, int M, int H, int hd,
-                            const int32_t* pos0, const int32_t* ntok_eff, float* part,
-                            int n_split_max, int max_len, void* out, hipStream_t s);
-int attn_chunk();  // cache positions per attention split
+hipError_t launch_attention_f32(const float* q, const float* kcache, const float* vcache,
+                                size_t row_stride, size_t head_stride, int B, int M, int H,
+                                int hd, const int32_t* pos0, const int32_t* ntok_eff,
+                                int max_len, float* out, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1);
 hipError_t launch_act(int dtype, int ffn_kind, const float* y, int R, int F, void* a,
                       hipStream_t s);
 
 // sampling
 hipError_t launch_accept_rows(const float* p_logits, const float* q_logits,
                               const int32_t* x_tilde, int B, int K, int V, SamplingKnobs kn,
-                              uint64_t seed, uint64_t round, int32_t* res_acc,
-                              int32_t* res_cand, int32_t* res_status, float* dbg_p,
-                              float* dbg_q, hipStream_t s);
+                              uint64_t seed, uint64_t round, const uint64_t* round_dev,
+                              int32_t* res_acc, int32_t* res_cand, int32_t* res_status,
+                              float* dbg_p, float* dbg_q, hipStream_t s);
 hipError_t launch_select(const int32_t* x_tilde, int B, int K, const int32_t* res_acc,
                          const int32_t* res_cand, const int32_t* res_status,
                          int32_t* out_tok, int32_t* n_out, int32_t* row_status,
                          int32_t* t_len, const int32_t* t_base, int32_t* d_len,
                          const int32_t* d_base, int32_t* pending, int32_t* n_pending,
-                         hipStream_t s);
+                         uint64_t* round_dev, hipStream_t s);
 hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t* n_in,
                                int step, int K, int V, SamplingKnobs kn, uint64_t seed,
-                               uint64_t round, int32_t* x_tilde, float* q_logits,
-                               hipStream_t s);
+                               uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
+                               float* q_logits, hipStream_t s);
 hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
                                const int32_t* x_tilde, int B, int K, int step,
                                int32_t* tokens, int32_t* n_tok, hipStream_t s);

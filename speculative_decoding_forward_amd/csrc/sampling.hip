@@ -292,9 +292,11 @@ template <int VPT>
 __global__ __launch_bounds__(VT) void k_accept_rows(
     const float* __restrict__ p_logits, const float* __restrict__ q_logits,
     const int32_t* __restrict__ x_tilde, int K, int V, SamplingKnobs kn, uint64_t seed,
-    uint64_t round, int32_t* __restrict__ res_acc, int32_t* __restrict__ res_cand,
-    int32_t* __restrict__ res_status, float* __restrict__ dbg_p, float* __restrict__ dbg_q) {
+    uint64_t round, const uint64_t* __restrict__ round_dev, int32_t* __restrict__ res_acc,
+    int32_t* __restrict__ res_cand, int32_t* __restrict__ res_status, float* __restrict__ dbg_p,
+    float* __restrict__ dbg_q) {
   __shared__ VocabLDS sh;
+  if (round_dev) round = *round_dev;
   const int b = blockIdx.x / (K + 1), j = blockIdx.x % (K + 1), tid = threadIdx.x;
   const bool has_q = j < K;
   float pv[VPT], qv[VPT];
@@ -362,8 +364,10 @@ __global__ void k_select(const int32_t* __restrict__ x_tilde, int B, int K,
                          const int32_t* __restrict__ res_status, int32_t* __restrict__ out_tok,
                          int32_t* __restrict__ n_out, int32_t* __restrict__ row_status,
                          int32_t* t_len, const int32_t* t_base, int32_t* d_len,
-                         const int32_t* d_base, int32_t* pending, int32_t* n_pending) {
+                         const int32_t* d_base, int32_t* pending, int32_t* n_pending,
+                         uint64_t* round_dev) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (round_dev && b == 0) *round_dev += 1;  // the rows of this round were decided
   if (b >= B) return;
   int fatal = 0;
   for (int j = 0; j <= K; ++j)
@@ -420,8 +424,10 @@ template <int VPT>
 __global__ __launch_bounds__(VT) void k_draft_sample(
     const float* __restrict__ logits, int M, const int32_t* __restrict__ n_in, int step,
     int K, int V, SamplingKnobs kn, uint64_t seed, uint64_t round,
-    int32_t* __restrict__ x_tilde, float* __restrict__ q_logits) {
+    const uint64_t* __restrict__ round_dev, int32_t* __restrict__ x_tilde,
+    float* __restrict__ q_logits) {
   __shared__ VocabLDS sh;
+  if (round_dev) round = *round_dev;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int last = step == 0 ? max(0, min(n_in[b], M) - 1) : 0;
   const float* row = logits + ((size_t)b * M + last) * V;
@@ -488,12 +494,12 @@ __global__ void k_rollback(int32_t* __restrict__ len, const int32_t* __restrict_
 
 hipError_t launch_accept_rows(const float* p_logits, const float* q_logits,
                               const int32_t* x_tilde, int B, int K, int V, SamplingKnobs kn,
-                              uint64_t seed, uint64_t round, int32_t* res_acc,
-                              int32_t* res_cand, int32_t* res_status, float* dbg_p,
-                              float* dbg_q, hipStream_t s) {
+                              uint64_t seed, uint64_t round, const uint64_t* round_dev,
+                              int32_t* res_acc, int32_t* res_cand, int32_t* res_status,
+                              float* dbg_p, float* dbg_q, hipStream_t s) {
   VPT_DISPATCH(V, (k_accept_rows<P><<<B * (K + 1), VT, 0, s>>>(
-                       p_logits, q_logits, x_tilde, K, V, kn, seed, round, res_acc, res_cand,
-                       res_status, dbg_p, dbg_q)));
+                       p_logits, q_logits, x_tilde, K, V, kn, seed, round, round_dev, res_acc,
+                       res_cand, res_status, dbg_p, dbg_q)));
   return hipGetLastError();
 }
 
@@ -502,19 +508,19 @@ hipError_t launch_select(const int32_t* x_tilde, int B, int K, const int32_t* re
                          int32_t* out_tok, int32_t* n_out, int32_t* row_status,
                          int32_t* t_len, const int32_t* t_base, int32_t* d_len,
                          const int32_t* d_base, int32_t* pending, int32_t* n_pending,
-                         hipStream_t s) {
+                         uint64_t* round_dev, hipStream_t s) {
   k_select<<<cdiv(B, 64), 64, 0, s>>>(x_tilde, B, K, res_acc, res_cand, res_status, out_tok,
                                       n_out, row_status, t_len, t_base, d_len, d_base,
-                                      pending, n_pending);
+                                      pending, n_pending, round_dev);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t* n_in,
                                int step, int K, int V, SamplingKnobs kn, uint64_t seed,
-                               uint64_t round, int32_t* x_tilde, float* q_logits,
-                               hipStream_t s) {
+                               uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
+                               float* q_logits, hipStream_t s) {
   VPT_DISPATCH(V, (k_draft_sample<P><<<B, VT, 0, s>>>(logits, M, n_in, step, K, V, kn, seed,
-                                                     round, x_tilde, q_logits)));
+                                                     round, round_dev, x_tilde, q_logits)));
   return hipGetLastError();
 }
 

@@ -8,7 +8,9 @@ One round ([CANON] listing "One speculative decoding loop"; [LENS] §2.1 steps 1
   3. accept / resample / bonus with in-place cache roll-back and the next round's
      pending tokens (spec_accept_resample).
 Every step runs in the HIP library; this class only owns the device buffers and issues
-the calls on one stream.  All state stays on the device between rounds.
+the calls on one stream.  All state stays on the device between rounds, including the
+round number (an int64 device counter advanced by the accept step), so one round can be
+captured as a HIP graph and replayed round after round (``capture`` / ``replay``).
 """
 import numpy as np
 import torch
@@ -45,6 +47,8 @@ class SpecDecoder:
         self.pending = torch.zeros((batch, 2), **i32)
         self.n_pending = torch.ones(batch, **i32)
         self.acc_ws = binding.accept_workspace(batch, K, device)
+        self.round_dev = torch.zeros(1, dtype=torch.int64, device=device)
+        self.graph = None
         self.prefill_logits = torch.zeros((batch, prefill_chunk, V), dtype=torch.float32,
                                           device=device)
 
@@ -65,11 +69,12 @@ class SpecDecoder:
         self.pending[:, 1] = -1
         self.n_pending.fill_(1)
 
-    def draft_phase(self, rnd, stream=None):
+    def draft_phase(self, rnd, stream=None, device_round=False):
+        rd = self.round_dev if device_round else None
         for j in range(self.K):
             binding.draft_step(self.draft, self.dkv, self.pending, self.n_pending, j, self.knobs,
                                self.seed, rnd, self.x_tilde, self.q_logits, self.ws_d,
-                               stream=stream)
+                               stream=stream, round_dev=rd)
 
     def verify_phase(self, stream=None):
         binding.verify_tokens(self.pending, self.n_pending, self.x_tilde, self.vtok,
@@ -77,14 +82,37 @@ class SpecDecoder:
         binding.verify_forward(self.target, self.tkv, self.vtok, self.p_logits, self.ws_t,
                                stream=stream)
 
-    def accept_phase(self, rnd, stream=None):
+    def accept_phase(self, rnd, stream=None, device_round=False):
         binding.accept_resample(self.p_logits, self.q_logits, self.x_tilde, self.knobs,
                                 self.seed, rnd, self.out_tok, self.n_out, self.row_status,
                                 self.acc_ws, tkv=self.tkv, dkv=self.dkv, pending=self.pending,
-                                n_pending=self.n_pending, stream=stream)
+                                n_pending=self.n_pending, stream=stream,
+                                round_dev=self.round_dev if device_round else None)
 
     def step(self, rnd, stream=None):
-        """One full round (asynchronous on the stream)."""
+        """One full round with round number `rnd` (asynchronous on the stream)."""
         self.draft_phase(rnd, stream)
         self.verify_phase(stream)
         self.accept_phase(rnd, stream)
+
+    def step_device_round(self, stream=None):
+        """One full round numbered by the device counter, which it then advances."""
+        self.draft_phase(0, stream, device_round=True)
+        self.verify_phase(stream)
+        self.accept_phase(0, stream, device_round=True)
+
+    def set_round(self, rnd):
+        self.round_dev.fill_(int(rnd))
+
+    def capture(self):
+        """Capture one device-numbered round as a HIP graph (nothing is executed)."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step_device_round()
+        self.graph = g
+        return g
+
+    def replay(self):
+        """Run the captured round once more (the device round counter numbers it)."""
+        self.graph.replay()

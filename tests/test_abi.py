@@ -59,7 +59,7 @@ def test_argument_checks_launch_nothing():
     smp = binding.Sampling(1.0, 0, 1.0)
     # null pointers -> invalid, before any launch
     st = lib.spec_accept_resample(None, None, None, 1, 1, 10, ctypes.byref(smp), 0, 0, None,
-                                  None, None, None, None, None, None, None, None, 0, None)
+                                  None, None, None, None, None, None, None, None, None, 0, None)
     assert st == binding.SPEC_E_INVALID
     assert lib.spec_verify_forward(None, None, None, None, 1, 1, None, None, None, 0,
                                    None) == binding.SPEC_E_INVALID

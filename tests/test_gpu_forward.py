@@ -96,7 +96,7 @@ def test_bf16_micro_ragged(kind, hd):
         if n:
             err = np.abs(g[b, :n] - o[b, :n]).max()
             print(f"{kind} hd={hd} row {b}: max |logit diff| = {err:.3e}")
-            assert err <= 1e-2
+            assert err <= 1e-2      # two narrow layers: within 1e-2 outright
         assert np.all(g[b, n:] == 0)
     assert np.array_equal(kv.len.cpu().numpy(), oc.len)
     data = kv.data().float().cpu().numpy()
@@ -138,6 +138,32 @@ def test_rollback():
     assert np.array_equal(kv.len.cpu().numpy(), [4, 10])
 
 
+def oracle_spread(fn):
+    """Run an oracle computation twice: as written (float64 values rounded straight to
+    bf16) and with every bf16 rounding taken from the float32-rounded value instead.
+    Both are correct readings of the spec; their difference is the spread that cascading
+    bf16 rounding flips alone produce."""
+    o1 = fn()
+    orig = omodel.round_bf16
+    try:
+        omodel.round_bf16 = lambda x: orig(np.asarray(x, np.float64).astype(np.float32))
+        o2 = fn()
+    finally:
+        omodel.round_bf16 = orig
+    return o1, np.abs(o2 - o1)
+
+
+def assert_bf16_logits(g, o, spread, what):
+    """bf16 logits: max |diff| within max(1e-2, 3x the oracle's own rounding spread) and
+    mean |diff| within max(1e-3, 3x the mean spread)."""
+    err = np.abs(g - o)
+    tol_max = max(1e-2, 3 * spread.max())
+    tol_mean = max(1e-3, 3 * spread.mean())
+    print(f"{what}: max |diff| {err.max():.3e} (oracle spread {spread.max():.3e}), "
+          f"mean {err.mean():.3e} (spread {spread.mean():.3e}), scale {np.abs(o).max():.2f}")
+    assert err.max() <= tol_max and err.mean() <= tol_mean
+
+
 def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
     """Verify pass of a workload's target (optionally only its first `layers` layers,
     same weights, full width and vocabulary) on a cache filled with seeded values that
@@ -152,45 +178,33 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
     kv.len.fill_(wl.ctx)
     new = synth.context_ids(seed + 9, B, K + 1, shape.vocab)
     g, st = gpu_forward(m, kv, new)
-    o = None
+    o = spread = None
     if with_oracle:
-        oc = omodel.KVCache(shape, B, max_len)
-        oc.fill(fill.float().cpu().numpy(), [wl.ctx] * B)
-        o = omodel.forward(shape, Wn, oc, new)
-    return g, o, st, shape, Wn, new, fill
+        fill_np = fill.float().cpu().numpy()
+
+        def run():
+            oc = omodel.KVCache(shape, B, max_len)
+            oc.fill(fill_np, [wl.ctx] * B)
+            return omodel.forward(shape, Wn, oc, new)
+
+        o, spread = oracle_spread(run)
+    return g, o, spread, st
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
-    layers of the target: logits within 1e-2 of the oracle."""
-    g, o, st, *_ = synthetic_kv_case(wl_name, B, K, layers=2)
-    err = np.abs(g - o).max()
-    print(f"{wl_name} B={B} K={K} 2 layers: max |logit diff| = {err:.3e}, "
-          f"scale {np.abs(o).max():.2f}")
-    assert err <= 1e-2 and np.all(st == 0)
-
-
-def test_full_depth_small_within_rounding_spread():
-    """All 24 layers of the small target.  Two correct bf16 pipelines drift apart by
-    cascading bf16 rounding flips; the oracle run with its rounding order changed
-    (fp64 -> fp32 -> bf16 instead of fp64 -> bf16) measures that spread.  The GPU must
-    be within 1e-2 of the oracle or within 3x that spread."""
-    g, o, st, shape, Wn, new, fill = synthetic_kv_case("small", 1, 4)
-    err = np.abs(g - o).max()
-    orig = omodel.round_bf16
-    try:
-        omodel.round_bf16 = lambda x: orig(np.asarray(x, np.float64).astype(np.float32))
-        wl = synth.WORKLOADS["small"]
-        oc = omodel.KVCache(shape, 1, wl.ctx + 5)
-        oc.fill(fill.float().cpu().numpy(), [wl.ctx])
-        o2 = omodel.forward(shape, Wn, oc, new)
-    finally:
-        omodel.round_bf16 = orig
-    spread = np.abs(o2 - o).max()
-    print(f"small 24 layers: GPU-oracle {err:.3e}, oracle rounding-order spread {spread:.3e}")
+    layers of the target."""
+    g, o, spread, st = synthetic_kv_case(wl_name, B, K, layers=2)
     assert np.all(st == 0)
-    assert err <= max(1e-2, 3 * spread)
+    assert_bf16_logits(g, o, spread, f"{wl_name} B={B} K={K} 2 layers")
+
+
+def test_full_depth_small():
+    """All 24 layers of the small target (context 512, K=4, B=1)."""
+    g, o, spread, st = synthetic_kv_case("small", 1, 4)
+    assert np.all(st == 0)
+    assert_bf16_logits(g, o, spread, "small 24 layers")
 
 
 @pytest.mark.parametrize("wl_name,B", [("small", 1), ("7b", 1), ("7b", 8)])

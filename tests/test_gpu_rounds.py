@@ -73,3 +73,23 @@ def test_draft_equal_target_accepts_all_on_gpu():
         torch.cuda.synchronize()
         assert np.all(dec.n_out.cpu().numpy() == wl.K + 1)
         assert torch.equal(dec.tkv.len, dec.dkv.len + 1)
+
+
+def test_graph_replay_matches_eager_rounds():
+    """One captured round replayed 8 times gives, round by round, the same draft tokens,
+    emitted tokens, lengths and pending tokens as eager rounds numbered the same way."""
+    wl = synth.WORKLOADS["tiny"]
+    eager, _ = build(wl, 2, seed=3)
+    graphed, _ = build(wl, 2, seed=3)
+    graphed.set_round(0)
+    graphed.capture()
+    for r in range(8):
+        eager.step(r)
+        graphed.replay()
+        torch.cuda.synchronize()
+        for name in ("x_tilde", "out_tok", "n_out", "pending", "n_pending", "row_status"):
+            assert torch.equal(getattr(eager, name), getattr(graphed, name)), (r, name)
+        assert torch.equal(eager.tkv.len, graphed.tkv.len) and torch.equal(eager.dkv.len,
+                                                                           graphed.dkv.len)
+        assert torch.equal(eager.p_logits, graphed.p_logits)
+        assert int(graphed.round_dev.item()) == r + 1
