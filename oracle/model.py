@@ -156,6 +156,13 @@ class KVCache:
         self.len = new_len.copy()
 
 
+def matmul(a, w):
+    """a [n, in] times a weight stored [out, in]: the forward's only contraction (a
+    library product in float64; a test may swap in a lower-precision accumulation to
+    measure how far a correct fp32-accumulating evaluation can drift)."""
+    return a @ w.T
+
+
 def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
     """Score new tokens on top of the cache and append their K/V.
 
@@ -189,7 +196,7 @@ def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
         for b in rows:
             n, s0, p = int(n_tok[b]), L0[b], pos[b]
             h = rb(rmsnorm(x[b], g1, c.norm_eps))
-            qkv = h @ wqkv.T
+            qkv = matmul(h, wqkv)
             q = qkv[:, :d].reshape(n, H, hd)
             k = qkv[:, d:2 * d].reshape(n, H, hd)
             v = qkv[:, 2 * d:].reshape(n, H, hd)
@@ -200,18 +207,18 @@ def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
             cache.v[l][b, :, s0:s0 + n] = v.transpose(1, 0, 2)
             o = attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], p)
             o = o.reshape(n, d)
-            xb = x[b] + rb(o) @ wo.T
+            xb = x[b] + matmul(rb(o), wo)
             h = rb(rmsnorm(xb, g2, c.norm_eps))
             if c.ffn_kind == "swiglu":
-                a = rb(silu(h @ wg.T) * (h @ wu.T))
-                xb = xb + a @ wd.T
+                a = rb(silu(matmul(h, wg)) * matmul(h, wu))
+                xb = xb + matmul(a, wd)
             else:
-                a = rb(gelu(h @ w1.T))
-                xb = xb + a @ w2.T
+                a = rb(gelu(matmul(h, w1)))
+                xb = xb + matmul(a, w2)
             x[b] = xb
     logits = np.zeros((B, M, c.vocab))
     head, gf = f64("head"), f64("norm_f")
     for b in rows:
-        logits[b, :n_tok[b]] = rb(rmsnorm(x[b], gf, c.norm_eps)) @ head.T
+        logits[b, :n_tok[b]] = matmul(rb(rmsnorm(x[b], gf, c.norm_eps)), head)
     cache.len = cache.len + n_tok
     return logits

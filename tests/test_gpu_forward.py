@@ -139,18 +139,25 @@ def test_rollback():
 
 
 def oracle_spread(fn):
-    """Run an oracle computation twice: as written (float64 values rounded straight to
-    bf16) and with every bf16 rounding taken from the float32-rounded value instead.
-    Both are correct readings of the spec; their difference is the spread that cascading
-    bf16 rounding flips alone produce."""
+    """Run an oracle computation as written and in two other evaluations that are just
+    as correct for a bf16 model with fp32 accumulation: every bf16 rounding taken from
+    the float32-rounded value, and every matrix product accumulated in float32.  The
+    largest elementwise difference from the first run is the spread that rounding and
+    accumulation order alone produce (bf16 rounding flips cascade through the layers)."""
     o1 = fn()
-    orig = omodel.round_bf16
+    orig_rb, orig_mm = omodel.round_bf16, omodel.matmul
     try:
-        omodel.round_bf16 = lambda x: orig(np.asarray(x, np.float64).astype(np.float32))
+        omodel.round_bf16 = lambda x: orig_rb(np.asarray(x, np.float64).astype(np.float32))
         o2 = fn()
     finally:
-        omodel.round_bf16 = orig
-    return o1, np.abs(o2 - o1)
+        omodel.round_bf16 = orig_rb
+    try:
+        omodel.matmul = lambda a, w: (np.asarray(a, np.float32) @
+                                      np.asarray(w, np.float32).T).astype(np.float64)
+        o3 = fn()
+    finally:
+        omodel.matmul = orig_mm
+    return o1, np.maximum(np.abs(o2 - o1), np.abs(o3 - o1))
 
 
 def assert_bf16_logits(g, o, spread, what):
