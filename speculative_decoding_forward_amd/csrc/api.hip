@@ -102,7 +102,8 @@ struct FwdWS {
   void* q;            // rotated queries [R, d]
   void* att;          // attention output [R, d]
   float* part;        // attention partials
-  double* ss_part;    // residual GEMM: per-workgroup row sums of squares [d/16, R]
+  float* ypart;       // residual GEMMs: Y [R, d] before it is added to x
+  double* rope_cs;    // RoPE (cos, sin) per row and frequency [R, hd/2, 2]
   float* logits;      // draft-step logits [R, V]
   size_t total;
 };
@@ -139,7 +140,8 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
                             ? (size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4
                             : 0);
   w.logits = (float*)take(R * V * 4);
-  w.ss_part = (double*)take(c.dtype == SPEC_DT_BF16 ? (d / 16) * R * 8 : 0);
+  w.ypart = (float*)take(c.dtype == SPEC_DT_BF16 ? (size_t)R * d * 4 : 0);
+  w.rope_cs = (double*)take(c.dtype == SPEC_DT_BF16 ? R * (size_t)(c.head_dim / 2) * 16 : 0);
   w.total = off;
   return w;
 }
@@ -228,8 +230,8 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
 
 // bf16 models: 7 kernels per layer.
 //   QKV GEMM (+ RoPE, q out, K/V append) -> attention (+ split merge) ->
-//   O GEMM (+ residual, row sums of squares) -> row norm -> up GEMM (+ SwiGLU / GELU)
-//   -> down GEMM (+ residual, row sums of squares) -> row norm (next layer's / final)
+//   O GEMM (K-split partials) -> residual add + row norm -> up GEMM (+ SwiGLU / GELU)
+//   -> down GEMM (K-split partials) -> residual add + row norm (next layer's / final)
 spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
                          const FwdWS& w, hipStream_t s) {
   const spec_model_cfg& c = m->cfg;
@@ -237,8 +239,8 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
-  SPEC_LAUNCH(launch_embed_norm(m->embed, c.dtype, w.tok_eff, R, d, m->layers[0].norm1,
-                                c.norm_eps, w.x, w.h, s));
+  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, c.norm_eps, w.x,
+                                w.h, w.pos0, M, hd, c.rope_theta, w.rope_cs, s));
   GemmArgs base{};
   base.R = R;
   base.M = M;
@@ -246,11 +248,10 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.pos0 = w.pos0;
   base.d = d;
   base.hd = hd;
-  base.theta = c.rope_theta;
+  base.rope_cs = w.rope_cs;
   base.row_stride = kv->row_stride;
   base.head_stride = kv->head_stride;
   base.max_len = kv->max_len;
-  base.ss_part = w.ss_part;
   base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
   for (int l = 0; l < c.n_layers; ++l) {
     const spec_model::Layer& L = m->layers[l];
@@ -285,12 +286,12 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.W = g.W2 = (const uint16_t*)L.wo;
       g.N = g.N1 = d;
       g.K = d;
-      g.C = w.x;
+      g.C = w.ypart;
       g.ldc = d;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
-      SPEC_LAUNCH(launch_rownorm(w.x, w.ss_part, d / 16, R, d, L.norm2, c.norm_eps,
-                                 (uint16_t*)w.h, s));
+      SPEC_LAUNCH(launch_resid_norm(w.x, w.ypart, R, d, L.norm2, c.norm_eps,
+                                    (uint16_t*)w.h, s));
     }
     {
       GemmArgs g = base;
@@ -320,13 +321,13 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.W = g.W2 = (const uint16_t*)L.w_down;
       g.N = g.N1 = d;
       g.K = F;
-      g.C = w.x;
+      g.C = w.ypart;
       g.ldc = d;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
-      SPEC_LAUNCH(launch_rownorm(w.x, w.ss_part, d / 16, R, d,
-                                 l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f,
-                                 c.norm_eps, (uint16_t*)w.h, s));
+      SPEC_LAUNCH(launch_resid_norm(w.x, w.ypart, R, d,
+                                    l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f,
+                                    c.norm_eps, (uint16_t*)w.h, s));
     }
   }
   GemmArgs g = base;

@@ -25,12 +25,14 @@
 //              the KV cache at the row's position
 //   SWIGLU     columns paired (gate n, up n): a = bf16(silu(g) * u)
 //   GELU       a = bf16(gelu(y)), erf form
-//   RESID      x += Y (fp32 residual stream) and per-workgroup row sums of squares of
-//              the new x (fp64), from which k_rownorm forms h = bf16(RMSNorm(x) * g), the
-//              next matrix's input
+//   RESID      partial Y of the workgroup's K split -> fp32 buffer; k_resid_norm then
+//              adds the splits to the residual stream x in split order and forms
+//              h = bf16(RMSNorm(x) * g), the next matrix's input
 //
 // fp32 path (small fp32 models): separate simple kernels, one wave per output column.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 #include <math.h>
 
 #include "common.h"
@@ -38,9 +40,17 @@
 
 namespace specdec {
 
-constexpr int GW = 8;        // waves per workgroup
-constexpr int GT = GW * 64;  // threads per workgroup
-constexpr int PF = 4;        // super-steps of W in flight per wave
+#ifndef SPEC_GEMM_WAVES
+#define SPEC_GEMM_WAVES 7  // streaming waves per workgroup (plus one epilogue wave)
+#endif
+#ifndef SPEC_GEMM_RING
+#define SPEC_GEMM_RING 2
+#endif
+#ifndef SPEC_GEMM_WPC
+#define SPEC_GEMM_WPC 2  // resident workgroups per compute unit the grid is sized for
+#endif
+constexpr int GW = SPEC_GEMM_WAVES;  // streaming waves per workgroup
+constexpr int GT = (GW + 1) * 64;    // threads per workgroup
 
 __device__ __forceinline__ bf16x8 ld8(const u16* p, bool ok) {
   if (!ok) return bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -55,36 +65,167 @@ __device__ __forceinline__ bf16x8 ld8_nt(const u16* p, bool ok) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Global column of local column c (0..15) of workgroup bx.
-__device__ __forceinline__ int gemm_col(const GemmArgs& g, int bx, int c) {
+// Rows of W behind tile t: local columns 0..7 are rows lo..lo+7, columns 8..15 rows
+// hi..hi+7 (returned as pointers to the row starts).
+//   QKV_ROPE  columns (i, i + hd/2) of one head and section, so RoPE pairs meet in a tile
+//   SWIGLU    gate rows 8t.. and up rows 8t.. (W2), so silu(g) * u meets in a tile
+//   others    rows 16t .. 16t + 15
+__device__ __forceinline__ void tile_rows(const GemmArgs& g, int t, const u16*& lo,
+                                          const u16*& hi) {
+  const size_t K = (size_t)g.K;
   switch (g.mode) {
     case EPI_QKV_ROPE: {
       const int half = g.hd >> 1, per_head = half / 8, per_sec = g.d / 16;
-      const int sec = bx / per_sec, rem = bx % per_sec;
-      const int h = rem / per_head, i0 = 8 * (rem % per_head);
-      return sec * g.d + h * g.hd + i0 + (c < 8 ? c : half + c - 8);
+      const int sec = t / per_sec, rem = t - sec * per_sec;
+      const int h = rem / per_head, i0 = 8 * (rem - h * per_head);
+      const size_t base = (size_t)sec * g.d + (size_t)h * g.hd + i0;
+      lo = g.W + base * K;
+      hi = g.W + (base + half) * K;
+      return;
     }
     case EPI_SWIGLU:
-      return (c < 8 ? 0 : g.N1) + 8 * bx + (c & 7);
+      lo = g.W + (size_t)(8 * t) * K;
+      hi = g.W2 + (size_t)(8 * t) * K;
+      return;
     default:
-      return bx * 16 + c;
+      lo = g.W + (size_t)(16 * t) * K;
+      hi = lo + 8 * K;
+      return;
   }
 }
 
-__device__ __forceinline__ const u16* gemm_wrow(const GemmArgs& g, int col) {
-  return col < g.N1 ? g.W + (size_t)col * g.K : g.W2 + (size_t)(col - g.N1) * g.K;
+// Per-tile epilogue, run by the workgroup's epilogue wave.  part[w][mt][lane] holds
+// wave w's MFMA accumulator fragment of row tile mt: lane l has rows 4(l/16)+e
+// (e = 0..3) of local column l%16.  The GW partials are summed in wave order.
+// rowinfo[rr] = (absolute position, flags) of row r0 + rr: flag 1 = a real token of its
+// sequence, flag 2 = its K/V may be written (real token and position < max_len).
+template <int MT>
+__device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int r0,
+                                                   const floatx4 (*part)[MT][64],
+                                                   const int2* rowinfo, int lane) {
+  const int nl = lane & 15, gq = lane >> 4, R = g.R, mode = g.mode;
+  const bool is_hi = nl >= 8;
+  int sec = 0, h = 0, i = 0;
+  const int half = g.hd >> 1;
+  if (mode == EPI_QKV_ROPE) {
+    const int per_head = half / 8, per_sec = g.d / 16;
+    sec = t / per_sec;
+    const int rem = t - sec * per_sec;
+    h = rem / per_head;
+    i = 8 * (rem - h * per_head) + (nl & 7);
+  }
+#pragma unroll 1
+  for (int mt = 0; mt < MT; ++mt) {
+    // rotation factors of this lane's four rows, loaded together (one latency)
+    double cs[4], sn[4];
+    if (mode == EPI_QKV_ROPE && sec < 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = min(r0 + mt * 16 + 4 * gq + e, R - 1);
+        const double2 c2 = *reinterpret_cast<const double2*>(g.rope_cs +
+                                                             ((size_t)r * half + i) * 2);
+        cs[e] = c2.x;
+        sn[e] = c2.y;
+      }
+    }
+    floatx4 v = part[0][mt][lane];
+#pragma unroll
+    for (int w = 1; w < GW; ++w) {
+      const floatx4 p = part[w][mt][lane];
+      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
+      const float y = v[e];
+      const float yp = __shfl_xor(y, 8);  // the paired column c ^ 8 of the same row
+      if (r >= R) continue;
+      switch (mode) {
+        case EPI_QKV_ROPE: {
+          const float lo = is_hi ? yp : y, hi = is_hi ? y : yp;
+          u16 o;
+          if (sec < 2) {
+            o = is_hi ? f32_to_bf16((float)((double)hi * cs[e] + (double)lo * sn[e]))
+                      : f32_to_bf16((float)((double)lo * cs[e] - (double)hi * sn[e]));
+          } else {
+            o = f32_to_bf16(y);
+          }
+          const int ii = is_hi ? i + half : i;
+          if (sec == 0) {
+            g.q_out[(size_t)r * g.d + h * g.hd + ii] = o;
+          } else {
+            const int2 info = rowinfo[rr];
+            if (info.y & 2) {
+              const int b = r / g.M;
+              ((sec == 1) ? g.kc : g.vc)[(size_t)b * g.row_stride + (size_t)h * g.head_stride +
+                                         (size_t)info.x * g.hd + ii] = o;
+            }
+          }
+          break;
+        }
+        case EPI_SWIGLU:
+          if (!is_hi)
+            g.act_out[(size_t)r * g.N1 + 8 * t + nl] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
+          break;
+        case EPI_GELU:
+          g.act_out[(size_t)r * g.N + 16 * t + nl] =
+              f32_to_bf16(0.5f * y * (1.f + erff(y * 0.70710678118654752f)));
+          break;
+        case EPI_STORE:
+          g.C[(size_t)r * g.ldc + 16 * t + nl] = (rowinfo[rr].y & 1) ? y : 0.f;
+          break;
+        default:  // EPI_RESID: Y -> C; the row-norm kernel adds it to x
+          g.C[(size_t)r * g.ldc + 16 * t + nl] = y;
+          break;
+      }
+    }
+  }
 }
 
+// Persistent weight-streaming GEMM.  Workgroup (bx, by) owns row block by (MT*16 rows
+// of A) and the column tiles bx, bx + G, bx + 2G, ... (G = gridDim.x).  It has GW
+// streaming waves and one epilogue wave.  The streaming waves split K: wave wv takes
+// 128-wide super-steps wv, wv + GW, ... of every tile, so its steps form one flat
+// stream over (tile, step) and its register ring of P steps runs across tile
+// boundaries.  At the end of a tile each streaming wave parks its accumulator in LDS
+// (double-buffered by tile parity) and meets the others at one barrier; the epilogue
+// wave then sums the partials and runs the epilogue (with its own global loads and
+// stores) while the streaming waves go on with the next tile.  A streaming wave thus
+// never waits on anything but its own weight loads.
 template <int MT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
-  constexpr int P = MT <= 2 ? 4 : 2;  // super-steps of W and A in flight per wave
-  __shared__ float red[GW][MT * 16][17];
+  constexpr int P = MT <= 2 ? SPEC_GEMM_RING : (SPEC_GEMM_RING > 2 ? 2 : SPEC_GEMM_RING);
+  __shared__ floatx4 part[2][GW][MT][64];
+  __shared__ int2 rowinfo[MT * 16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int bx = blockIdx.x;
+  const int bx = blockIdx.x, G = gridDim.x;
   const int r0 = blockIdx.y * (MT * 16);
+  const int nt = (g.ntiles - bx + G - 1) / G;  // tiles of this workgroup (>= 1)
+  if (wv == GW) {
+    for (int rr = lane; rr < MT * 16; rr += 64) {
+      const int r = r0 + rr;
+      int2 info{0, 0};
+      if (r < g.R) {
+        const int b = r / g.M, j = r - b * g.M;
+        const int n = g.ntok_eff ? g.ntok_eff[b] : g.M;
+        const int pos = (g.pos0 ? g.pos0[b] : 0) + j;
+        info = int2{pos, (j < n ? 1 : 0) | (j < n && pos < g.max_len ? 2 : 0)};
+      }
+      rowinfo[rr] = info;
+    }
+    wave_lds_sync();
+    for (int ct = 0; ct < nt; ++ct) {
+      __syncthreads();
+      gemm_tile_epilogue<MT>(g, bx + ct * G, r0, part[ct & 1], rowinfo, lane);
+    }
+    return;
+  }
   const int nl = lane & 15, gq = lane >> 4;
-  const int K = g.K, R = g.R;
-  const u16* wrow = gemm_wrow(g, gemm_col(g, bx, nl)) + 8 * gq;
+  const int R = g.R, nsuper = g.K >> 7;
+  const int S = (nsuper + GW - 1) / GW;  // steps per tile, the same for every wave
+  const bool wact = wv < nsuper;
+  const int last_step = wact ? (nsuper - 1 - wv) / GW : 0;
+  const size_t lane_row = (size_t)(nl & 7) * g.K + 8 * gq;
   const u16* arow[MT];
   bool aok[MT];
 #pragma unroll
@@ -97,31 +238,40 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // K is a multiple of 128.  Wave wv owns super-steps wv, wv + GW, ...; every wave runs
-  // the same trip count S = ceil(nsuper / GW) so the loop body has no branches (the
-  // compiler then keeps every slot of the ring in flight across iterations).  A step
-  // past the wave's last one re-reads the wave's last W segment (already in cache, no
-  // HBM traffic) and multiplies it by a zero A fragment.
-  const int nsuper = K >> 7;
-  const int S = (nsuper + GW - 1) / GW;
-  const int last_step = nsuper > wv ? (nsuper - 1 - wv) / GW : 0;
   bf16x8 wf[P][4];
   bf16x8 af[P][MT][4];
-  // invalid A fragments are read from a zeroed 16-byte block (an address select, so the
-  // loaded data is never waited on before the MFMA that uses it)
   const u16* zblk = g.zeros;
-  auto issue = [&](int slot, int step) {
-    const bool valid = step <= last_step && wv < nsuper;
-    // waves without any step of their own read the first segment (in bounds) times 0
-    const int kb = wv < nsuper ? (wv + (valid ? step : last_step) * GW) * 128 : 0;
+  // issue stream: tile iteration it, step is; a step past the wave's last one in a tile,
+  // or past the workgroup's last tile, re-reads an in-bounds W segment (cache hit) and
+  // pairs it with zero A fragments, so every wave runs the same branch-free schedule.
+  int it = 0, is = 0;
+  const u16* wp;
+  {
+    const u16 *lo, *hi;
+    tile_rows(g, bx, lo, hi);
+    wp = (nl < 8 ? lo : hi) + lane_row;
+  }
+  auto issue = [&](int slot) {
+    const bool valid = is <= last_step && wact && it < nt;
+    const int kb = wact ? (wv + (is <= last_step ? is : last_step) * GW) * 128 : 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wf[slot][s] = ld8_nt(wrow + kb + 32 * s, true);
+    for (int s = 0; s < 4; ++s) wf[slot][s] = ld8_nt(wp + kb + 32 * s, true);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         af[slot][mt][s] = ld8((valid && aok[mt]) ? arow[mt] + kb + 32 * s : zblk, true);
+    if (++is == S) {
+      is = 0;
+      ++it;
+      if (it < nt) {
+        const u16 *lo, *hi;
+        tile_rows(g, bx + it * G, lo, hi);
+        wp = (nl < 8 ? lo : hi) + lane_row;
+      }
+    }
   };
+  int ct = 0, cs = 0;  // consume stream: tile iteration, step
   auto consume = [&](int slot) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -129,129 +279,56 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
       for (int s = 0; s < 4; ++s)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mt][s], wf[slot][s],
                                                           acc[mt], 0, 0, 0);
-  };
-  const int T = (S + P - 1) / P;  // rounds of P steps
+    if (++cs == S) {
+      cs = 0;
+      if (ct < nt) {
 #pragma unroll
-  for (int u = 0; u < P; ++u) issue(u, u);
-  for (int t = 0; t + 1 < T; ++t) {
+        for (int mt = 0; mt < MT; ++mt) part[ct & 1][wv][mt][lane] = acc[mt];
+        __syncthreads();
+      }
+      ++ct;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // Rounds of P steps; the last round's refills read in-bounds W past the end (cache
+  // hits, never consumed) so that the loop body is the only copy of the tile code.
+  const int F = nt * S;  // steps of this wave
+  const int T = (F + P - 1) / P;
+#pragma unroll
+  for (int u = 0; u < P; ++u) issue(u);
+  for (int t = 0; t < T; ++t) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       consume(u);
-      issue(u, (t + 1) * P + u);
+      issue(u);
       // keep each refill right behind the use of its slot (no drain per round)
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-#pragma unroll
-  for (int u = 0; u < P; ++u) consume(u);
-  // D layout: lane holds rows 4*gq .. 4*gq+3 of each tile, column nl
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[wv][mt * 16 + 4 * gq + e][nl] = acc[mt][e];
-  __syncthreads();
-  // sum the wave partials in place (fixed order) into red[0]
-  for (int idx = threadIdx.x; idx < MT * 16 * 16; idx += GT) {
-    const int rr = idx >> 4, c = idx & 15;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < GW; ++w) v += red[w][rr][c];
-    red[0][rr][c] = v;
-  }
-  __syncthreads();
-
-  const int mode = g.mode;
-  if (mode == EPI_QKV_ROPE || mode == EPI_SWIGLU) {
-    // pairs: local columns c and c + 8
-    for (int idx = threadIdx.x; idx < MT * 16 * 8; idx += GT) {
-      const int rr = idx >> 3, c = idx & 7;
-      const int r = r0 + rr;
-      if (r >= R) continue;
-      const float lo = red[0][rr][c], hi = red[0][rr][c + 8];
-      if (mode == EPI_SWIGLU) {
-        const int col = 8 * bx + c;
-        const float v = lo / (1.f + expf(-lo)) * hi;
-        g.act_out[(size_t)r * g.N1 + col] = f32_to_bf16(v);
-        continue;
-      }
-      const int half = g.hd >> 1, per_head = half / 8, per_sec = g.d / 16;
-      const int sec = bx / per_sec, rem = bx % per_sec;
-      const int h = rem / per_head, i = 8 * (rem % per_head) + c;
-      const int b = r / g.M, j = r % g.M;
-      const int pos = g.pos0[b] + j;
-      u16 o0, o1;
-      if (sec < 2) {
-        const double inv_freq = pow((double)g.theta, -2.0 * (double)i / (double)g.hd);
-        double sn, cs;
-        sincos((double)pos * inv_freq, &sn, &cs);
-        o0 = f32_to_bf16((float)((double)lo * cs - (double)hi * sn));
-        o1 = f32_to_bf16((float)((double)hi * cs + (double)lo * sn));
-      } else {
-        o0 = f32_to_bf16(lo);
-        o1 = f32_to_bf16(hi);
-      }
-      if (sec == 0) {
-        u16* qo = g.q_out + (size_t)r * g.d + h * g.hd;
-        qo[i] = o0;
-        qo[i + half] = o1;
-      } else if (j < g.ntok_eff[b] && pos < g.max_len) {
-        u16* cp = (sec == 1 ? g.kc : g.vc) + (size_t)b * g.row_stride +
-                  (size_t)h * g.head_stride + (size_t)pos * g.hd;
-        cp[i] = o0;
-        cp[i + half] = o1;
-      }
-    }
-    return;
-  }
-  if (mode != EPI_RESID) {
-    for (int idx = threadIdx.x; idx < MT * 16 * 16; idx += GT) {
-      const int rr = idx >> 4, c = idx & 15;
-      const int r = r0 + rr;
-      if (r >= R) continue;
-      const int col = bx * 16 + c;
-      const float v = red[0][rr][c];
-      if (mode == EPI_STORE) {
-        const bool pad = g.ntok_eff && (r % g.M) >= g.ntok_eff[r / g.M];
-        g.C[(size_t)r * g.ldc + col] = pad ? 0.f : v;
-      } else {  // EPI_GELU
-        g.act_out[(size_t)r * g.N + col] =
-            f32_to_bf16(0.5f * v * (1.f + erff(v * 0.70710678118654752f)));
-      }
-    }
-    return;
-  }
-  // EPI_RESID: x += Y, plus this workgroup's share of each row's sum of squares of the
-  // new x (one wave per row, lanes 0..15 over the 16 columns) in ss_part[bx][r] (fp64);
-  // the row-norm kernel that follows turns them into the next matrix's input.
-  for (int rr = wv; rr < MT * 16; rr += GW) {
-    const int r = r0 + rr;
-    if (r >= R) continue;
-    double sq = 0.0;
-    if (lane < 16) {
-      float* p = g.C + (size_t)r * g.ldc + bx * 16 + lane;
-      const float nv = *p + red[0][rr][lane];
-      *p = nv;
-      sq = (double)nv * nv;
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-    if (lane == 0) g.ss_part[(size_t)bx * R + r] = sq;
-  }
 }
 
-// h[r] = bf16(x[r] * rsqrt(sum_sq[r] / d + eps) * g): one 256-thread block per row; the
-// row's sum of squares is the fixed-order sum of the GEMM workgroups' partials.
-__global__ __launch_bounds__(256) void k_rownorm(const float* __restrict__ x,
-                                                 const double* __restrict__ ss_part, int nparts,
-                                                 int R, int d, const float* __restrict__ gain,
-                                                 float eps, u16* __restrict__ h) {
+// Residual update and RMSNorm of the next matrix's input, one 256-thread block per row:
+//   x[r] += y[r];  h[r] = bf16(x[r] * g / rms(x[r]))
+// with the sum of squares and the scaling in fp64.
+__global__ __launch_bounds__(256) void k_resid_norm(float* __restrict__ x,
+                                                    const float* __restrict__ y, int R, int d,
+                                                    const float* __restrict__ gain, float eps,
+                                                    u16* __restrict__ h) {
   __shared__ double red[4];
   const int r = blockIdx.x;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
+  const float4* yr = reinterpret_cast<const float4*>(y + (size_t)r * d);
   double sq = 0.0;
-  for (int j = threadIdx.x; j < nparts; j += 256) sq += ss_part[(size_t)j * R + r];
+  for (int i = threadIdx.x; i < d / 4; i += 256) {
+    float4 v = xr[i];
+    const float4 p = yr[i];
+    v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    xr[i] = v;
+    sq += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  }
   sq = block_sum(sq, red);
   const double inv = 1.0 / sqrt(sq / d + (double)eps);
-  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)r * d);
   const float4* gr = reinterpret_cast<const float4*>(gain);
   uint2* hr = reinterpret_cast<uint2*>(h + (size_t)r * d);
   for (int i = threadIdx.x; i < d / 4; i += 256) {
@@ -264,9 +341,9 @@ __global__ __launch_bounds__(256) void k_rownorm(const float* __restrict__ x,
   }
 }
 
-hipError_t launch_rownorm(const float* x, const double* ss_part, int nparts, int R, int d,
-                          const float* gain, float eps, uint16_t* h, hipStream_t s) {
-  k_rownorm<<<R, 256, 0, s>>>(x, ss_part, nparts, R, d, gain, eps, h);
+hipError_t launch_resid_norm(float* x, const float* y, int R, int d, const float* gain,
+                             float eps, uint16_t* h, hipStream_t s) {
+  k_resid_norm<<<R, 256, 0, s>>>(x, y, R, d, gain, eps, h);
   return hipGetLastError();
 }
 
@@ -313,19 +390,42 @@ int gemm_blocks_x(const GemmArgs& g) {
   }
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Grid: G persistent workgroups per row block, G chosen so that the tiles divide as
+// evenly as possible (every workgroup gets ceil(tiles / G) or one fewer).
+hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  GemmArgs g = g0;
+  g.ntiles = gemm_blocks_x(g);
   const int tiles = cdiv(g.R, 16);
-  const int bx = gemm_blocks_x(g);
+  const int rowblocks = tiles <= 3 ? 1 : cdiv(g.R, 64);
+  const int gmax = std::max(1, device_cus() * SPEC_GEMM_WPC / rowblocks);
+  const int per = cdiv(g.ntiles, gmax);
+  const int G = cdiv(g.ntiles, per);
   if (tiles <= 1) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<1>, dim3(bx, 1), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<1>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
   } else if (tiles <= 2) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<2>, dim3(bx, 1), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
   } else if (tiles <= 3) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<3>, dim3(bx, 1), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<3>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
   } else {
-    hipExtLaunchKernelGGL(k_gemm_bf16<4>, dim3(bx, cdiv(g.R, 64)), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<4>, dim3(G, rowblocks), dim3(GT), 0, s, e0, e1, 0, g);
   }
   return hipGetLastError();
 }
+
 
 }  // namespace specdec

@@ -53,14 +53,15 @@ struct GemmArgs {
   const uint16_t* W2;  // rows >= N1 (SwiGLU up matrix), else == W
   int N1;
   int R, N, K, mode;
-  float* C;  // STORE: logits; RESID: residual stream x
+  int ntiles;  // column tiles (set by the launcher)
+  float* C;  // STORE: logits [R, N]; RESID: Y [R, N], added to the residual stream later
   int ldc;
   const int32_t* ntok_eff;  // [B] tokens per sequence (rows past it are padding)
   int M;                    // rows per sequence
   // QKV_ROPE
   const int32_t* pos0;
   int d, hd;
-  float theta;
+  const double* rope_cs;  // [R][hd/2][2] (cos, sin) of each row's rotation angles
   uint16_t* q_out;
   uint16_t* kc;
   uint16_t* vc;
@@ -68,19 +69,19 @@ struct GemmArgs {
   int max_len;
   // SWIGLU / GELU
   uint16_t* act_out;
-  // RESID
-  double* ss_part;        // [N/16, R] per-workgroup sums of squares
   const uint16_t* zeros;  // >= 16 zero bytes (device)
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-hipError_t launch_rownorm(const float* x, const double* ss_part, int nparts, int R, int d,
-                          const float* gain, float eps, uint16_t* h, hipStream_t s);
+hipError_t launch_resid_norm(float* x, const float* y, int R, int d,
+                             const float* gain, float eps, uint16_t* h, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
                            int N, int K, float* C, int accumulate, const int32_t* ntok_eff,
                            int M, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-hipError_t launch_embed_norm(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
-                             const float* g, float eps, float* x, void* h, hipStream_t s);
+hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
+                             const float* g, float eps, float* x, void* h,
+                             const int32_t* pos0, int M, int hd, float theta, double* rope_cs,
+                             hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                                  size_t row_stride, size_t head_stride, int B, int M, int H,
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,

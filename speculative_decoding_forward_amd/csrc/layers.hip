@@ -68,14 +68,29 @@ __global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok
 }
 
 // bf16 models: x[r, :] = E[tok[r], :] (fp32) and h = bf16(RMSNorm(x) * g) of the first
-// layer in one pass.  One block (256 threads) per row.
+// layer in one pass; also the row's RoPE rotation table rope_cs[r][i] = (cos, sin) of
+// pos * theta^(-2i/hd), i < hd/2, in fp64, which every layer's QKV epilogue reads (the
+// position of row r = b*M + j is pos0[b] + j).  One block (256 threads) per row.
 __global__ __launch_bounds__(256) void k_embed_norm(const u16* __restrict__ E,
                                                     const int32_t* __restrict__ tok, int d,
                                                     const float* __restrict__ g, float eps,
-                                                    float* __restrict__ x, u16* __restrict__ h) {
+                                                    float* __restrict__ x, u16* __restrict__ h,
+                                                    const int32_t* __restrict__ pos0, int M,
+                                                    int hd, float theta,
+                                                    double* __restrict__ rope_cs) {
   __shared__ double red[4];
   const int r = blockIdx.x;
   const u16* e = E + (size_t)tok[r] * d;
+  const int half = hd >> 1;
+  if (threadIdx.x < half) {
+    const int i = threadIdx.x;
+    const double pos = (double)(pos0[r / M] + r % M);
+    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)hd);
+    double sn, cs;
+    sincos(pos * inv_freq, &sn, &cs);
+    rope_cs[((size_t)r * half + i) * 2] = cs;
+    rope_cs[((size_t)r * half + i) * 2 + 1] = sn;
+  }
   double s = 0.0;
   for (int i = threadIdx.x; i < d; i += 256) {
     const float v = bf16_to_f32(e[i]);
@@ -537,10 +552,13 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
 
 int attn_split() { return ASPLIT; }
 
-hipError_t launch_embed_norm(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
-                             const float* g, float eps, float* x, void* h, hipStream_t s) {
-  (void)dtype;
-  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, eps, x, (u16*)h);
+hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
+                             const float* g, float eps, float* x, void* h,
+                             const int32_t* pos0, int M, int hd, float theta, double* rope_cs,
+                             hipStream_t s) {
+  if (hd / 2 > 256) return hipErrorInvalidValue;
+  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, eps, x, (u16*)h, pos0, M, hd,
+                                 theta, rope_cs);
   return hipGetLastError();
 }
 
