@@ -93,19 +93,40 @@ typedef struct spec_kv spec_kv;       /* opaque */
 /* Number of weight pointers spec_model_create expects for `cfg`. */
 int spec_model_n_weights(const spec_model_cfg* cfg);
 
-/* Bind a model to caller-owned device weights (the library keeps the pointers, copies
- * nothing).  `weights` (host array of device pointers) in this order:
+/* Device bytes a model of `cfg` allocates for its own copy of the weights (0 for an
+ * invalid cfg). */
+size_t spec_model_bytes(const spec_model_cfg* cfg);
+
+/* Create a model: the library allocates spec_model_bytes(cfg) of device memory and
+ * keeps its own copy of every tensor there, the bf16 matrices rearranged into the
+ * tile order the verify GEMM streams (column tiles of 16 weight rows, each tile one
+ * contiguous block in MFMA operand order), so each weight byte is read from HBM once
+ * in fully used 1 KB wave loads ([ZSM] "The cost of one token is the cost of reading
+ * the weights").  `weights` (host array of device pointers, or NULL) in this order:
  *   embed [V,d], head [V,d], norm_f [d] (fp32),
  *   then per layer: norm1 [d] (fp32), wqkv [3d,d] (rows: q heads | k heads | v heads),
  *   wo [d,d], norm2 [d] (fp32), then SwiGLU: wgate [F,d], wup [F,d], wdown [d,F]
  *   or GELU: w1 [F,d], w2 [d,F].
- * Matrices and embeddings are bf16 for SPEC_DT_BF16 and fp32 for SPEC_DT_F32.
+ * Matrices and embeddings are bf16 for SPEC_DT_BF16 and fp32 for SPEC_DT_F32, row-major
+ * [out, in].  With weights given, every tensor is copied before the call returns (on
+ * the null stream, which is synchronised) and the caller may free its buffers; with
+ * weights == NULL the storage is left unset for spec_model_load_weight.
  * Returns SPEC_E_INVALID for a bad shape, count or null pointer; SPEC_E_UNSUPPORTED
- * for a shape the kernels are not built for (bf16: head_dim 64 or 128 and d_model,
- * d_ffn, vocab multiples of 16; f32: even head_dim <= 128) or a device that is not
- * gfx950.  *out receives the handle. */
+ * for a shape the kernels are not built for (bf16: head_dim 64 or 128, d_model and
+ * d_ffn multiples of 128, vocab a multiple of 16; f32: even head_dim <= 128) or a
+ * device that is not gfx950; SPEC_E_CAPACITY if the device allocation fails.
+ * *out receives the handle. */
 spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
                               int n_weights, spec_model** out);
+
+/* Copy tensor `index` (canonical order above; device pointer `src` in the layout
+ * given there) into the model, asynchronously on `stream` (NULL: the null stream):
+ * `src` must stay valid until the stream has passed this call.  Lets a loader stage
+ * one tensor at a time (peak memory: the model plus one tensor).  SPEC_E_INVALID for
+ * a bad index or null pointer, SPEC_E_HIP if the copy cannot be queued. */
+spec_status spec_model_load_weight(spec_model* m, int index, const void* src, void* stream);
+
+/* Free the model and its device copy of the weights. */
 spec_status spec_model_destroy(spec_model* m);
 
 /* ------------------------------------------------------------------ KV cache ------ */

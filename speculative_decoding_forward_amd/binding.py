@@ -20,7 +20,8 @@ FFN = {"gelu": 0, "swiglu": 1}
 DT = {"f32": 0, "bf16": 1}
 
 SYMBOLS = [
-    "spec_model_n_weights", "spec_model_create", "spec_model_destroy", "spec_kv_bytes",
+    "spec_model_n_weights", "spec_model_bytes", "spec_model_create", "spec_model_load_weight",
+    "spec_model_destroy", "spec_kv_bytes",
     "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_rollback",
     "spec_workspace_bytes", "spec_verify_forward", "spec_draft_step",
     "spec_accept_workspace_bytes", "spec_accept_resample", "spec_verify_tokens",
@@ -76,7 +77,9 @@ def load(path=None):
     smp = ctypes.POINTER(Sampling)
     sig = {
         "spec_model_n_weights": (I32, [cfgp]),
+        "spec_model_bytes": (SZ, [cfgp]),
         "spec_model_create": (I32, [cfgp, ctypes.POINTER(P), I32, ctypes.POINTER(P)]),
+        "spec_model_load_weight": (I32, [P, I32, P, P]),
         "spec_model_destroy": (I32, [P]),
         "spec_kv_bytes": (SZ, [cfgp, I32, I32]),
         "spec_kv_create": (I32, [cfgp, I32, I32, P, SZ, P, ctypes.POINTER(P)]),
@@ -129,19 +132,35 @@ def _alloc(nbytes, device):
 
 
 class Model:
-    """A model bound to device weights (dict name -> tensor, canonical order)."""
+    """A model holding its own device copy of the weights.
 
-    def __init__(self, shape: "synth.ModelShape", weights):
+    weights: dict name -> device tensor (canonical names and shapes of the shape), copied
+    (and, for bf16 matrices, rearranged into GEMM tiles) at construction; the caller may
+    drop them afterwards.  weights=None allocates the storage only: fill it tensor by
+    tensor with ``load_weight`` (a loader's peak memory is then the model plus one
+    tensor)."""
+
+    def __init__(self, shape: "synth.ModelShape", weights=None):
         lib = load()
         self.shape = shape
         self.cfg = ModelCfg.from_shape(shape)
-        names = shape.weight_names()
-        self.weights = [weights[n].contiguous() for n in names]
-        arr = (P * len(names))(*[t.data_ptr() for t in self.weights])
+        self.names = shape.weight_names()
         h = P()
-        _check(lib.spec_model_create(ctypes.byref(self.cfg), arr, len(names), ctypes.byref(h)),
+        if weights is None:
+            arr, n = None, 0
+        else:
+            ts = [weights[nm].contiguous() for nm in self.names]
+            arr, n = (P * len(ts))(*[t.data_ptr() for t in ts]), len(ts)
+        _check(lib.spec_model_create(ctypes.byref(self.cfg), arr, n, ctypes.byref(h)),
                "spec_model_create")
         self.handle = h
+
+    def load_weight(self, name, tensor, stream=None):
+        """Copy one tensor (canonical name) into the model on `stream`; the tensor must
+        stay alive until the stream has passed the copy."""
+        t = tensor.contiguous()
+        _check(load().spec_model_load_weight(self.handle, self.names.index(name), _ptr(t),
+                                             _stream(stream)), "spec_model_load_weight")
 
     def __del__(self):
         if getattr(self, "handle", None) and _LIB is not None:

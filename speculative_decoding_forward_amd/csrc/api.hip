@@ -53,8 +53,9 @@ bool cfg_valid(const spec_model_cfg* c) {
 
 bool cfg_supported(const spec_model_cfg* c) {
   if (c->dtype == SPEC_DT_BF16) {
+    // GEMM contraction dims in 128-wide super-steps, output dims in 16-column tiles
     if (c->head_dim != 64 && c->head_dim != 128) return false;
-    if (c->d_model % 16 || c->d_ffn % 16 || c->vocab % 16) return false;
+    if (c->d_model % 128 || c->d_ffn % 128 || c->vocab % 16) return false;
   } else {
     if (c->head_dim % 2 || c->head_dim > 128) return false;
   }
@@ -262,7 +263,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.mode = EPI_QKV_ROPE;
       g.A = (const uint16_t*)w.h;
       g.lda = d;
-      g.W = g.W2 = (const uint16_t*)L.wqkv;
+      g.W = (const uint16_t*)L.wqkv;
       g.N = g.N1 = 3 * d;
       g.K = d;
       g.q_out = (uint16_t*)w.q;
@@ -283,7 +284,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.mode = EPI_RESID;
       g.A = (const uint16_t*)w.att;
       g.lda = d;
-      g.W = g.W2 = (const uint16_t*)L.wo;
+      g.W = (const uint16_t*)L.wo;
       g.N = g.N1 = d;
       g.K = d;
       g.C = w.ypart;
@@ -302,12 +303,10 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.W = (const uint16_t*)L.w_up;
       if (c.ffn_kind == SPEC_FFN_SWIGLU) {
         g.mode = EPI_SWIGLU;
-        g.W2 = (const uint16_t*)L.w_up2;
         g.N1 = F;
         g.N = 2 * F;
       } else {
         g.mode = EPI_GELU;
-        g.W2 = g.W;
         g.N = g.N1 = F;
       }
       Ev ev = timed(g_timing.gemm);
@@ -318,7 +317,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.mode = EPI_RESID;
       g.A = (const uint16_t*)w.a;
       g.lda = F;
-      g.W = g.W2 = (const uint16_t*)L.w_down;
+      g.W = (const uint16_t*)L.w_down;
       g.N = g.N1 = d;
       g.K = F;
       g.C = w.ypart;
@@ -334,7 +333,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   g.mode = EPI_STORE;
   g.A = (const uint16_t*)w.h;
   g.lda = d;
-  g.W = g.W2 = (const uint16_t*)m->head;
+  g.W = (const uint16_t*)m->head;
   g.N = g.N1 = V;
   g.K = d;
   g.C = logits;
@@ -385,48 +384,165 @@ int spec_model_n_weights(const spec_model_cfg* cfg) {
   return 3 + cfg->n_layers * (cfg->ffn_kind == SPEC_FFN_SWIGLU ? 7 : 6);
 }
 
+namespace {
+
+// Tensor i of the canonical order: its shape, where it lives in the model's store and
+// how it is written there.
+struct TensorSlot {
+  int rows, cols;   // source shape [rows, cols] (norm gains: [1, d])
+  bool fp32;        // stored as fp32 (norm gains, and every tensor of an fp32 model)
+  int pack;         // -1 plain copy, else a PACK_* mode
+  int ntiles;       // packed tiles (pack >= 0)
+  size_t offset;    // byte offset of the tensor's storage in the store
+  size_t bytes;     // storage bytes (for a pair half: the whole pair)
+};
+
+// Lay the model out; returns the store size and fills slots (canonical order) if given.
+size_t model_layout(const spec_model_cfg& c, TensorSlot* slots) {
+  const int d = c.d_model, F = c.d_ffn, V = c.vocab, L = c.n_layers;
+  const bool bf = c.dtype == SPEC_DT_BF16, swiglu = c.ffn_kind == SPEC_FFN_SWIGLU;
+  const size_t e = bf ? 2 : 4;
+  size_t off = 0;
+  int i = 0;
+  auto put = [&](int rows, int cols, bool gain, int pack, int ntiles) {
+    TensorSlot t{rows, cols, gain || !bf, bf && !gain ? pack : -1, ntiles, off, 0};
+    t.bytes = (size_t)rows * cols * (t.fp32 ? 4 : e);
+    off += align_up(t.bytes);
+    if (slots) slots[i] = t;
+    ++i;
+  };
+  put(V, d, false, -1, 0);               // embed (gathered by token, kept as given)
+  put(V, d, false, PACK_PLAIN, V / 16);  // head
+  put(1, d, true, -1, 0);                // norm_f
+  for (int l = 0; l < L; ++l) {
+    put(1, d, true, -1, 0);                         // norm1
+    put(3 * d, d, false, PACK_QKV, 3 * d / 16);     // wqkv
+    put(d, d, false, PACK_PLAIN, d / 16);           // wo
+    put(1, d, true, -1, 0);                         // norm2
+    if (swiglu && bf) {
+      // gate and up share one packed block of F/8 tiles
+      TensorSlot g{F, d, false, PACK_PAIR_LO, F / 8, off, (size_t)2 * F * d * e};
+      TensorSlot u = g;
+      u.pack = PACK_PAIR_HI;
+      off += align_up(g.bytes);
+      if (slots) {
+        slots[i] = g;
+        slots[i + 1] = u;
+      }
+      i += 2;
+    } else if (swiglu) {
+      put(F, d, false, -1, 0);  // wgate
+      put(F, d, false, -1, 0);  // wup
+    } else {
+      put(F, d, false, PACK_PLAIN, F / 16);  // w1
+    }
+    put(d, F, false, PACK_PLAIN, d / 16);   // wdown / w2
+  }
+  return off;
+}
+
+}  // namespace
+
+size_t spec_model_bytes(const spec_model_cfg* cfg) {
+  if (!cfg_valid(cfg)) return 0;
+  return model_layout(*cfg, nullptr);
+}
+
 spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
                               int n_weights, spec_model** out) {
-  if (!cfg_valid(cfg) || !weights || !out) return SPEC_E_INVALID;
-  if (n_weights != spec_model_n_weights(cfg)) return SPEC_E_INVALID;
-  for (int i = 0; i < n_weights; ++i)
-    if (!weights[i]) return SPEC_E_INVALID;
+  if (!cfg_valid(cfg) || !out) return SPEC_E_INVALID;
+  if (weights) {
+    if (n_weights != spec_model_n_weights(cfg)) return SPEC_E_INVALID;
+    for (int i = 0; i < n_weights; ++i)
+      if (!weights[i]) return SPEC_E_INVALID;
+  }
   if (!cfg_supported(cfg)) return SPEC_E_UNSUPPORTED;
   if (!device_is_gfx950()) return SPEC_E_UNSUPPORTED;
+  const int n = spec_model_n_weights(cfg);
+  std::vector<TensorSlot> slots(n);
+  const size_t bytes = model_layout(*cfg, slots.data());
   spec_model* m = new (std::nothrow) spec_model;
   if (!m) return SPEC_E_INVALID;
   m->cfg = *cfg;
   m->layers = new (std::nothrow) spec_model::Layer[cfg->n_layers];
+  m->store = nullptr;
+  m->store_bytes = bytes;
   if (!m->layers) {
     delete m;
     return SPEC_E_INVALID;
   }
+  hipError_t err = hipMalloc(&m->store, bytes);
+  if (err != hipSuccess) {
+    g_last_hip_error.store((int)err);
+    delete[] m->layers;
+    delete m;
+    return SPEC_E_CAPACITY;
+  }
+  char* base = (char*)m->store;
   int i = 0;
-  m->embed = weights[i++];
-  m->head = weights[i++];
-  m->norm_f = (const float*)weights[i++];
+  auto at = [&]() { return (const void*)(base + slots[i++].offset); };
+  m->embed = at();
+  m->head = at();
+  m->norm_f = (const float*)at();
   for (int l = 0; l < cfg->n_layers; ++l) {
     spec_model::Layer& L = m->layers[l];
-    L.norm1 = (const float*)weights[i++];
-    L.wqkv = weights[i++];
-    L.wo = weights[i++];
-    L.norm2 = (const float*)weights[i++];
+    L.norm1 = (const float*)at();
+    L.wqkv = at();
+    L.wo = at();
+    L.norm2 = (const float*)at();
+    L.w_up = at();
+    L.w_up2 = nullptr;
     if (cfg->ffn_kind == SPEC_FFN_SWIGLU) {
-      L.w_up = weights[i++];
-      L.w_up2 = weights[i++];
-      L.w_down = weights[i++];
-    } else {
-      L.w_up = weights[i++];
-      L.w_up2 = nullptr;
-      L.w_down = weights[i++];
+      const void* up = at();
+      if (cfg->dtype != SPEC_DT_BF16) L.w_up2 = up;
+    }
+    L.w_down = at();
+  }
+  if (weights) {
+    for (int k = 0; k < n; ++k) {
+      const spec_status st = spec_model_load_weight(m, k, weights[k], nullptr);
+      if (st != SPEC_OK) {
+        spec_model_destroy(m);
+        return st;
+      }
+    }
+    err = hipStreamSynchronize(nullptr);
+    if (err != hipSuccess) {
+      g_last_hip_error.store((int)err);
+      spec_model_destroy(m);
+      return SPEC_E_HIP;
     }
   }
   *out = m;
   return SPEC_OK;
 }
 
+spec_status spec_model_load_weight(spec_model* m, int index, const void* src, void* stream) {
+  if (!m || !src) return SPEC_E_INVALID;
+  const int n = spec_model_n_weights(&m->cfg);
+  if (index < 0 || index >= n) return SPEC_E_INVALID;
+  std::vector<TensorSlot> slots(n);
+  model_layout(m->cfg, slots.data());
+  const TensorSlot& t = slots[index];
+  hipStream_t s = (hipStream_t)stream;
+  char* dst = (char*)m->store + t.offset;
+  hipError_t err;
+  if (t.pack < 0) {
+    err = hipMemcpyAsync(dst, src, t.bytes, hipMemcpyDeviceToDevice, s);
+  } else {
+    err = launch_pack_bf16((const uint16_t*)src, t.cols, t.pack, m->cfg.d_model,
+                           m->cfg.head_dim, t.ntiles, (uint16_t*)dst, s);
+  }
+  if (err != hipSuccess) {
+    g_last_hip_error.store((int)err);
+    return SPEC_E_HIP;
+  }
+  return SPEC_OK;
+}
+
 spec_status spec_model_destroy(spec_model* m) {
   if (!m) return SPEC_E_INVALID;
+  if (m->store) hipFree(m->store);
   delete[] m->layers;
   delete m;
   return SPEC_OK;

@@ -41,7 +41,7 @@
 namespace specdec {
 
 #ifndef SPEC_GEMM_WAVES
-#define SPEC_GEMM_WAVES 7  // streaming waves per workgroup (plus one epilogue wave)
+#define SPEC_GEMM_WAVES 4  // streaming waves per workgroup (plus one epilogue wave)
 #endif
 #ifndef SPEC_GEMM_RING
 #define SPEC_GEMM_RING 2
@@ -65,33 +65,72 @@ __device__ __forceinline__ bf16x8 ld8_nt(const u16* p, bool ok) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Rows of W behind tile t: local columns 0..7 are rows lo..lo+7, columns 8..15 rows
-// hi..hi+7 (returned as pointers to the row starts).
-//   QKV_ROPE  columns (i, i + hd/2) of one head and section, so RoPE pairs meet in a tile
-//   SWIGLU    gate rows 8t.. and up rows 8t.. (W2), so silu(g) * u meets in a tile
-//   others    rows 16t .. 16t + 15
-__device__ __forceinline__ void tile_rows(const GemmArgs& g, int t, const u16*& lo,
-                                          const u16*& hi) {
-  const size_t K = (size_t)g.K;
-  switch (g.mode) {
-    case EPI_QKV_ROPE: {
-      const int half = g.hd >> 1, per_head = half / 8, per_sec = g.d / 16;
-      const int sec = t / per_sec, rem = t - sec * per_sec;
-      const int h = rem / per_head, i0 = 8 * (rem - h * per_head);
-      const size_t base = (size_t)sec * g.d + (size_t)h * g.hd + i0;
-      lo = g.W + base * K;
-      hi = g.W + (base + half) * K;
-      return;
+// Packed weight layout.  A matrix is stored as a sequence of column tiles, each the
+// 16 weight rows behind 16 output columns; tile t, super-step j (k in [128j, 128j+128)),
+// MFMA slice s (k in [128j + 32s, +32)) and lane l hold, contiguously,
+//   row(t, l % 16)[128j + 32s + 8(l / 16) .. +8]
+// at element offset (((t * K/128 + j) * 4 + s) * 64 + l) * 8, i.e. exactly the B operand
+// of v_mfma_f32_16x16x32_bf16 for that slice.  Every wave load is then 1 KB contiguous
+// and a tile is one contiguous 32*K-byte block.  Which weight row sits behind local
+// column c of tile t depends on the epilogue that consumes the tile:
+//   QKV_ROPE  c < 8: row base + c, c >= 8: row base + hd/2 + c - 8 of the fused [3d, d]
+//             matrix, base = sec*d + h*hd + i0 (RoPE pairs (i, i + hd/2) meet in a tile)
+//   SWIGLU    c < 8: gate row 8t + c, c >= 8: up row 8t + c - 8 (silu(g) * u meets)
+//   others    row 16t + c
+struct QkvTile {
+  int sec, h, i0;  // section (0 q, 1 k, 2 v), head, first rotation index of the tile
+};
+__device__ __forceinline__ QkvTile qkv_tile(int t, int d, int hd) {
+  const int half = hd >> 1, per_head = half / 8, per_sec = d / 16;
+  QkvTile q;
+  q.sec = t / per_sec;
+  const int rem = t - q.sec * per_sec;
+  q.h = rem / per_head;
+  q.i0 = 8 * (rem - q.h * per_head);
+  return q;
+}
+
+// Pack src [rows, K] (row-major bf16) into the tile layout above.  mode: PACK_PLAIN,
+// PACK_QKV (src is the fused [3d, d] matrix), PACK_PAIR_LO / PACK_PAIR_HI (src fills the
+// c < 8 / c >= 8 half of tiles of 8 rows).  One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void k_pack_bf16(const u16* __restrict__ src, int K, int mode,
+                                                   int d, int hd, int ntiles,
+                                                   u16* __restrict__ dst) {
+  const int J = K >> 7;
+  const size_t chunks = (size_t)ntiles * J * 256;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks;
+       q += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(q & 63), s = (int)((q >> 6) & 3);
+    const size_t tj = q >> 8;
+    const int j = (int)(tj % J), t = (int)(tj / J);
+    const int c = l & 15;
+    int row;
+    if (mode == PACK_QKV) {
+      const QkvTile qt = qkv_tile(t, d, hd);
+      const int base = qt.sec * d + qt.h * hd + qt.i0;
+      row = c < 8 ? base + c : base + (hd >> 1) + c - 8;
+    } else if (mode == PACK_PAIR_LO) {
+      if (c >= 8) continue;
+      row = 8 * t + c;
+    } else if (mode == PACK_PAIR_HI) {
+      if (c < 8) continue;
+      row = 8 * t + c - 8;
+    } else {
+      row = 16 * t + c;
     }
-    case EPI_SWIGLU:
-      lo = g.W + (size_t)(8 * t) * K;
-      hi = g.W2 + (size_t)(8 * t) * K;
-      return;
-    default:
-      lo = g.W + (size_t)(16 * t) * K;
-      hi = lo + 8 * K;
-      return;
+    const int k = 128 * j + 32 * s + 8 * (l >> 4);
+    *reinterpret_cast<uint4*>(dst + q * 8) =
+        *reinterpret_cast<const uint4*>(src + (size_t)row * K + k);
   }
+}
+
+hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
+                            uint16_t* dst, hipStream_t s) {
+  if (K % 128 || ntiles < 1) return hipErrorInvalidValue;
+  const size_t chunks = (size_t)ntiles * (K >> 7) * 256;
+  const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 8192);
+  k_pack_bf16<<<blocks, 256, 0, s>>>(src, K, mode, d, hd, ntiles, dst);
+  return hipGetLastError();
 }
 
 // Per-tile epilogue, run by the workgroup's epilogue wave.  part[w][mt][lane] holds
@@ -108,11 +147,10 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
   int sec = 0, h = 0, i = 0;
   const int half = g.hd >> 1;
   if (mode == EPI_QKV_ROPE) {
-    const int per_head = half / 8, per_sec = g.d / 16;
-    sec = t / per_sec;
-    const int rem = t - sec * per_sec;
-    h = rem / per_head;
-    i = 8 * (rem - h * per_head) + (nl & 7);
+    const QkvTile qt = qkv_tile(t, g.d, g.hd);
+    sec = qt.sec;
+    h = qt.h;
+    i = qt.i0 + (nl & 7);
   }
 #pragma unroll 1
   for (int mt = 0; mt < MT; ++mt) {
@@ -225,7 +263,7 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   const int S = (nsuper + GW - 1) / GW;  // steps per tile, the same for every wave
   const bool wact = wv < nsuper;
   const int last_step = wact ? (nsuper - 1 - wv) / GW : 0;
-  const size_t lane_row = (size_t)(nl & 7) * g.K + 8 * gq;
+  const size_t tile_elems = (size_t)nsuper * 2048;  // one packed tile
   const u16* arow[MT];
   bool aok[MT];
 #pragma unroll
@@ -245,17 +283,13 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   // or past the workgroup's last tile, re-reads an in-bounds W segment (cache hit) and
   // pairs it with zero A fragments, so every wave runs the same branch-free schedule.
   int it = 0, is = 0;
-  const u16* wp;
-  {
-    const u16 *lo, *hi;
-    tile_rows(g, bx, lo, hi);
-    wp = (nl < 8 ? lo : hi) + lane_row;
-  }
+  const u16* wp = g.W + (size_t)bx * tile_elems + 8 * lane;
   auto issue = [&](int slot) {
     const bool valid = is <= last_step && wact && it < nt;
-    const int kb = wact ? (wv + (is <= last_step ? is : last_step) * GW) * 128 : 0;
+    const int js = wact ? wv + (is <= last_step ? is : last_step) * GW : 0;  // super-step
+    const int kb = js * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wf[slot][s] = ld8_nt(wp + kb + 32 * s, true);
+    for (int s = 0; s < 4; ++s) wf[slot][s] = ld8_nt(wp + js * 2048 + 512 * s, true);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -264,11 +298,7 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     if (++is == S) {
       is = 0;
       ++it;
-      if (it < nt) {
-        const u16 *lo, *hi;
-        tile_rows(g, bx + it * G, lo, hi);
-        wp = (nl < 8 ? lo : hi) + lane_row;
-      }
+      if (it < nt) wp += (size_t)G * tile_elems;
     }
   };
   int ct = 0, cs = 0;  // consume stream: tile iteration, step

@@ -9,18 +9,22 @@
 
 struct spec_model {
   spec_model_cfg cfg;
-  // device pointers, canonical order (see spec_model_create)
-  const void* embed;
-  const void* head;
+  // The model owns one device allocation holding its copy of every tensor: bf16
+  // matrices packed into GEMM tiles, the rest (embedding, norm gains, fp32 matrices)
+  // stored as given.
+  void* store;
+  size_t store_bytes;
+  const void* embed;   // [V, d] as given
+  const void* head;    // bf16: packed tiles of 16 vocabulary rows; f32: [V, d]
   const float* norm_f;
   struct Layer {
     const float* norm1;
-    const void* wqkv;
+    const void* wqkv;    // bf16: packed (RoPE-paired tiles); f32: [3d, d]
     const void* wo;
     const float* norm2;
-    const void* w_up;    // SwiGLU: wgate; GELU: w1
-    const void* w_up2;   // SwiGLU: wup;   GELU: unused
-    const void* w_down;  // SwiGLU: wdown; GELU: w2
+    const void* w_up;    // bf16 SwiGLU: packed gate/up pair tiles; GELU: w1.  f32: wgate / w1
+    const void* w_up2;   // f32 SwiGLU: wup; otherwise unused
+    const void* w_down;  // wdown / w2
   };
   Layer* layers;
 };
@@ -49,9 +53,8 @@ enum { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_GELU 
 struct GemmArgs {
   const uint16_t* A;  // [R, K] bf16 activations
   int lda;
-  const uint16_t* W;   // [N1, K] (rows < N1)
-  const uint16_t* W2;  // rows >= N1 (SwiGLU up matrix), else == W
-  int N1;
+  const uint16_t* W;  // packed column tiles (see the packed layout in gemm.hip)
+  int N1;             // SWIGLU: gate/up width F (output row stride); else N
   int R, N, K, mode;
   int ntiles;  // column tiles (set by the launcher)
   float* C;  // STORE: logits [R, N]; RESID: Y [R, N], added to the residual stream later
@@ -73,6 +76,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };
+hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
+                            uint16_t* dst, hipStream_t s);
 hipError_t launch_resid_norm(float* x, const float* y, int R, int d,
                              const float* gain, float eps, uint16_t* h, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
