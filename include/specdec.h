@@ -132,8 +132,13 @@ spec_status spec_model_destroy(spec_model* m);
 /* ------------------------------------------------------------------ KV cache ------ */
 
 /* Bytes of the KV arena for `batch` rows of up to `max_len` positions.  Layout:
- * [n_layers][batch][2 (K,V)][n_heads][max_len][head_dim] elements (bf16 for bf16
- * models, fp32 for f32), followed by 256-byte aligned per-row bookkeeping. */
+ * [n_layers][batch][2 (K,V)][n_heads] head regions, then 256-byte aligned per-row
+ * bookkeeping and, for bf16 models, the RoPE table (cos, sin of every position's
+ * angles, fp64).  fp32 models: a head region is [max_len][head_dim] (natural order).
+ * bf16 models: a head region holds roundup(max_len, 32) positions in the order the
+ * attention's matrix-core products read them (K in blocks of 16 positions, V
+ * transposed in blocks of 32); use spec_kv_import / spec_kv_export to move positions
+ * in natural order. */
 size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len);
 
 /* Bind a cache to a caller-owned arena of at least spec_kv_bytes() and to a caller-
@@ -143,9 +148,18 @@ spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, vo
                            size_t arena_bytes, int32_t* len, spec_kv** out);
 spec_status spec_kv_destroy(spec_kv* kv);
 
-/* Device pointer to the start of the arena's K/V element block (for seeding a cache
- * with precomputed contents, e.g. a long prefilled context). */
+/* Device pointer to the start of the arena's K/V element block. */
 void* spec_kv_data(spec_kv* kv);
+
+/* Write positions [0, n_pos) of every row, layer and head from `src` (device, natural
+ * order [n_layers][batch][2][n_heads][n_pos][head_dim], the model's element type),
+ * asynchronously on `stream`; for seeding a cache with precomputed contents, e.g. a
+ * long prefilled context.  Lengths are not changed.  SPEC_E_INVALID for a null pointer
+ * or n_pos outside [0, max_len]. */
+spec_status spec_kv_import(spec_kv* kv, const void* src, int n_pos, void* stream);
+
+/* Read positions [0, n_pos) into `dst` in the natural order of spec_kv_import. */
+spec_status spec_kv_export(spec_kv* kv, void* dst, int n_pos, void* stream);
 
 /* Roll back: len[b] <- min(len[b], max(new_len[b], 0)).  Entries past the new length
  * become stale and are overwritten by the next append.  [LENS] §2.1: drafts after the

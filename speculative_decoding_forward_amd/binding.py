@@ -22,7 +22,8 @@ DT = {"f32": 0, "bf16": 1}
 SYMBOLS = [
     "spec_model_n_weights", "spec_model_bytes", "spec_model_create", "spec_model_load_weight",
     "spec_model_destroy", "spec_kv_bytes",
-    "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_rollback",
+    "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_import", "spec_kv_export",
+    "spec_kv_rollback",
     "spec_workspace_bytes", "spec_verify_forward", "spec_draft_step",
     "spec_accept_workspace_bytes", "spec_accept_resample", "spec_verify_tokens",
     "spec_status_str", "spec_last_hip_error", "spec_abi_version", "spec_timing_enable",
@@ -85,6 +86,8 @@ def load(path=None):
         "spec_kv_create": (I32, [cfgp, I32, I32, P, SZ, P, ctypes.POINTER(P)]),
         "spec_kv_destroy": (I32, [P]),
         "spec_kv_data": (P, [P]),
+        "spec_kv_import": (I32, [P, P, I32, P]),
+        "spec_kv_export": (I32, [P, P, I32, P]),
         "spec_kv_rollback": (I32, [P, P, P]),
         "spec_workspace_bytes": (SZ, [cfgp, I32, I32, I32]),
         "spec_verify_forward": (I32, [P, P, P, P, I32, I32, P, P, P, SZ, P]),
@@ -198,12 +201,29 @@ class KVCache:
             self.handle = None
 
     def data(self):
-        """The K/V block viewed as [L, B, 2, H, max_len, hd] (bf16 or fp32)."""
+        """The raw K/V element block (bf16 caches hold it in the attention's packed
+        order; use import_/export for natural order)."""
         s = self.shape
         dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
-        n = s.n_layers * self.batch * 2 * s.n_heads * self.max_len * s.head_dim
-        flat = self.arena[: n * (2 if s.dtype == "bf16" else 4)].view(dt)
-        return flat.view(s.n_layers, self.batch, 2, s.n_heads, self.max_len, s.head_dim)
+        cap = (self.max_len + 31) // 32 * 32 if s.dtype == "bf16" else self.max_len
+        n = s.n_layers * self.batch * 2 * s.n_heads * cap * s.head_dim
+        return self.arena[: n * (2 if s.dtype == "bf16" else 4)].view(dt)
+
+    def import_(self, src, stream=None):
+        """Write positions [0, n) of every row from src [L, B, 2, H, n, hd] (device)."""
+        t = src.contiguous()
+        _check(load().spec_kv_import(self.handle, _ptr(t), t.shape[4], _stream(stream)),
+               "spec_kv_import")
+
+    def export(self, n, stream=None):
+        """Positions [0, n) of every row as [L, B, 2, H, n, hd] (natural order)."""
+        s = self.shape
+        dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+        out = torch.empty((s.n_layers, self.batch, 2, s.n_heads, n, s.head_dim), dtype=dt,
+                          device=self.arena.device)
+        _check(load().spec_kv_export(self.handle, _ptr(out), n, _stream(stream)),
+               "spec_kv_export")
+        return out
 
     def rollback(self, new_len, stream=None):
         _check(load().spec_kv_rollback(self.handle, _ptr(new_len), _stream(stream)),

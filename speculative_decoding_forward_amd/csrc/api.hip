@@ -104,7 +104,6 @@ struct FwdWS {
   void* att;          // attention output [R, d]
   float* part;        // attention partials
   float* ypart;       // residual GEMMs: Y [R, d] before it is added to x
-  double* rope_cs;    // RoPE (cos, sin) per row and frequency [R, hd/2, 2]
   float* logits;      // draft-step logits [R, V]
   size_t total;
 };
@@ -115,7 +114,8 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   const size_t e = elt_bytes(c);
   const size_t d = c.d_model, F = c.d_ffn, V = c.vocab;
   const size_t ffn_out = c.ffn_kind == SPEC_FFN_SWIGLU ? 2 * F : F;
-  const size_t nsplit = (size_t)cdiv(max_len, attn_split());
+  // attention splits: at most one per 4 blocks of 32 positions (any call shape)
+  const size_t nsplit = (size_t)cdiv(cdiv(max_len, 32), 4);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -129,7 +129,7 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.ntok2 = (int32_t*)take(B * 4);
   // attention completion counters [B*H*ceil(M/8)] followed by 64 zero words; prep
   // clears all of them at the start of every forward
-  w.n_counters = B * c.n_heads * cdiv(M, 8) + 64;
+  w.n_counters = B * c.n_heads * attn_groups(M) + 64;
   w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
   w.h = take(R * d * e);
@@ -142,7 +142,6 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
                             : 0);
   w.logits = (float*)take(R * V * 4);
   w.ypart = (float*)take(c.dtype == SPEC_DT_BF16 ? (size_t)R * d * 4 : 0);
-  w.rope_cs = (double*)take(c.dtype == SPEC_DT_BF16 ? R * (size_t)(c.head_dim / 2) * 16 : 0);
   w.total = off;
   return w;
 }
@@ -241,7 +240,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
   SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, c.norm_eps, w.x,
-                                w.h, w.pos0, M, hd, c.rope_theta, w.rope_cs, s));
+                                w.h, s));
   GemmArgs base{};
   base.R = R;
   base.M = M;
@@ -249,7 +248,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.pos0 = w.pos0;
   base.d = d;
   base.hd = hd;
-  base.rope_cs = w.rope_cs;
+  base.rope_cs = kv->rope;
   base.row_stride = kv->row_stride;
   base.head_stride = kv->head_stride;
   base.max_len = kv->max_len;
@@ -548,10 +547,17 @@ spec_status spec_model_destroy(spec_model* m) {
   return SPEC_OK;
 }
 
+// RoPE table of a bf16 cache: (cos, sin) of pos * theta^(-2i/hd) for every position.
+size_t rope_table_bytes(const spec_model_cfg& c, int max_len) {
+  return c.dtype == SPEC_DT_BF16 ? (size_t)max_len * (c.head_dim / 2) * 16 : 0;
+}
+
 size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len) {
   if (!cfg_valid(cfg) || batch < 1 || max_len < 1) return 0;
-  const size_t n = (size_t)cfg->n_layers * batch * 2 * cfg->n_heads * max_len * cfg->head_dim;
-  return align_up(n * elt_bytes(*cfg)) + align_up((size_t)batch * 4);
+  const size_t cap = cfg->dtype == SPEC_DT_BF16 ? kv_capacity(max_len) : max_len;
+  const size_t n = (size_t)cfg->n_layers * batch * 2 * cfg->n_heads * cap * cfg->head_dim;
+  return align_up(n * elt_bytes(*cfg)) + align_up((size_t)batch * 4) +
+         align_up(rope_table_bytes(*cfg, max_len));
 }
 
 spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, void* arena,
@@ -568,12 +574,36 @@ spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, vo
   kv->data = arena;
   kv->len = len;
   const size_t hd = cfg->head_dim, H = cfg->n_heads;
-  kv->head_stride = (size_t)max_len * hd;
+  kv->head_stride =
+      (size_t)(cfg->dtype == SPEC_DT_BF16 ? kv_capacity(max_len) : max_len) * hd;
   kv->kv_stride = H * kv->head_stride;
   kv->row_stride = 2 * kv->kv_stride;
   kv->layer_stride = (size_t)batch * kv->row_stride;
   const size_t n = (size_t)cfg->n_layers * kv->layer_stride;
   kv->base = (int32_t*)((char*)arena + align_up(n * elt_bytes(*cfg)));
+  kv->rope = nullptr;
+  if (cfg->dtype == SPEC_DT_BF16) {
+    // rotation factors in fp64, evaluated once on the host: angle pos * theta^(-2i/hd)
+    kv->rope = (double*)((char*)kv->base + align_up((size_t)batch * 4));
+    const int half = cfg->head_dim / 2;
+    std::vector<double> tab((size_t)max_len * half * 2);
+    for (int i = 0; i < half; ++i) {
+      const double inv_freq =
+          std::pow((double)cfg->rope_theta, -2.0 * (double)i / (double)cfg->head_dim);
+      for (int p = 0; p < max_len; ++p) {
+        const double a = (double)p * inv_freq;
+        tab[((size_t)p * half + i) * 2] = std::cos(a);
+        tab[((size_t)p * half + i) * 2 + 1] = std::sin(a);
+      }
+    }
+    const hipError_t err =
+        hipMemcpy(kv->rope, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice);
+    if (err != hipSuccess) {
+      g_last_hip_error.store((int)err);
+      delete kv;
+      return SPEC_E_HIP;
+    }
+  }
   *out = kv;
   return SPEC_OK;
 }
@@ -585,6 +615,39 @@ spec_status spec_kv_destroy(spec_kv* kv) {
 }
 
 void* spec_kv_data(spec_kv* kv) { return kv ? kv->data : nullptr; }
+
+namespace {
+spec_status kv_transfer(spec_kv* kv, void* nat, int n_pos, void* stream, int to_cache) {
+  if (!kv || !nat || n_pos < 0 || n_pos > kv->max_len) return SPEC_E_INVALID;
+  const spec_model_cfg& c = kv->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  if (c.dtype == SPEC_DT_BF16) {
+    err = launch_kv_convert((uint16_t*)kv->data, (uint16_t*)nat, c.n_layers, kv->batch,
+                            c.n_heads, c.head_dim, n_pos, kv->layer_stride, kv->row_stride,
+                            kv->kv_stride, kv->head_stride, to_cache, s);
+  } else {
+    // fp32 caches keep the natural layout: one strided copy
+    const size_t w = (size_t)n_pos * c.head_dim * 4;
+    const size_t heads = (size_t)c.n_layers * kv->batch * 2 * c.n_heads;
+    if (w == 0) return SPEC_OK;
+    err = to_cache ? hipMemcpy2DAsync(kv->data, kv->head_stride * 4, nat, w, w, heads,
+                                      hipMemcpyDeviceToDevice, s)
+                   : hipMemcpy2DAsync(nat, w, kv->data, kv->head_stride * 4, w, heads,
+                                      hipMemcpyDeviceToDevice, s);
+  }
+  if (err != hipSuccess) return hip_fail(err);
+  return SPEC_OK;
+}
+}  // namespace
+
+spec_status spec_kv_import(spec_kv* kv, const void* src, int n_pos, void* stream) {
+  return kv_transfer(kv, const_cast<void*>(src), n_pos, stream, 1);
+}
+
+spec_status spec_kv_export(spec_kv* kv, void* dst, int n_pos, void* stream) {
+  return kv_transfer(kv, dst, n_pos, stream, 0);
+}
 
 spec_status spec_kv_rollback(spec_kv* kv, const int32_t* new_len, void* stream) {
   if (!kv || !new_len) return SPEC_E_INVALID;

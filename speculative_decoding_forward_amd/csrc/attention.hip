@@ -1,0 +1,382 @@
+// KV-cache attention of the verify pass (bf16 models): the K+1 query rows of each
+// sequence attend causally over its cache ([LENS] §2.1 step 2: one target call scores
+// every drafted position; [GC] "How It Works": the verify pass runs the draft tokens
+// through the target in parallel).  A query at cache position p sees positions t <= p.
+//
+// Cache layout (per layer, row b, head h; the arrangement inside a head region of
+// cap = roundup(max_len, 32) positions x hd elements):
+//   K: blocks of 16 positions; block k, slice s (dims 32s .. 32s+31) and lane l hold
+//      K[16k + l%16][32s + 8(l/16) .. +8] -- the A operand of v_mfma_f32_16x16x32_bf16
+//      for S^T = K Q^T;
+//   V: blocks of 32 positions; block k, dim tile u (dims 16u .. 16u+15) and lane l hold
+//      V[32k + key(l/16, e)][16u + l%16] for e = 0..7 with key(g, e) = 4g + e (e < 4)
+//      or 16 + 4g + e - 4 -- the B operand of O = P V, in the key order in which the
+//      S^T fragments leave the first product (so P never moves between lanes).
+// Every wave load is therefore 1 KB contiguous.
+//
+// Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
+// (b, h) and one group of up to 16 queries; its 4 waves take the blocks round-robin,
+// keep two blocks of K and V in flight, and run an online softmax per query.  The
+// wave states merge in LDS; with more than one split the workgroup partial goes to
+// global memory and the last workgroup of (b, h, qg) to finish merges them in split
+// order and writes the bf16 output.  P enters the second product as bf16 hi + lo
+// parts (two MFMAs), which keeps its value to ~16 bits.
+#include <hip/hip_ext.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace specdec {
+
+constexpr int AW = 4;    // waves per workgroup
+constexpr int AQ = 16;   // queries per group
+constexpr int AKB = 32;  // keys per block
+
+__device__ __forceinline__ bf16x8 ldfrag(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+template <int HD>
+__global__ __launch_bounds__(AW * 64) void k_attn_bf16(
+    const u16* __restrict__ q, int M, int H, const u16* __restrict__ kc,
+    const u16* __restrict__ vc, size_t row_stride, size_t head_stride,
+    const int32_t* __restrict__ pos0, const int32_t* __restrict__ ntok_eff,
+    float* __restrict__ part, unsigned* __restrict__ counters, int nsplit, int npw,
+    u16* __restrict__ out) {
+  constexpr int NS = HD / 32;  // K slices (MFMAs per 16-key tile)
+  constexpr int NT = HD / 16;  // dim tiles of O
+  __shared__ float wm[AW][AQ], wl[AW][AQ];
+  __shared__ float wo[AW][AQ][HD + 1];
+  __shared__ int last_flag;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int NG = cdiv(M, AQ);
+  const int b = blockIdx.z / NG, qg = blockIdx.z % NG;
+  const int h = blockIdx.y, split = blockIdx.x;
+  const int nq = ntok_eff[b];
+  const int p0 = pos0[b];
+  const int len_end = p0 + nq;
+  const int bps = AW * npw;  // blocks per split
+  const int nblk = cdiv(len_end, AKB);
+  const int n_active = cdiv(nblk, bps);
+  const int d = H * HD;
+  const int jend = min(M, qg * AQ + AQ);  // rows of this query group
+  if (qg * AQ >= nq) {
+    // no query of this row in this group: the first split writes the padding rows
+    if (split == 0)
+      for (int idx = threadIdx.x; idx < (jend - qg * AQ) * HD; idx += AW * 64)
+        out[((size_t)b * M + qg * AQ + idx / HD) * d + h * HD + idx % HD] = 0;
+    return;
+  }
+  if (split >= n_active) return;  // uniform over the workgroup
+  const u16* kh = kc + (size_t)b * row_stride + (size_t)h * head_stride;
+  const u16* vh = vc + (size_t)b * row_stride + (size_t)h * head_stride;
+  const float scale = 1.0f / sqrtf((float)HD);
+
+  // query fragments (B operand of S^T = K Q^T): query column nl, dims 32s + 8g .. +8;
+  // columns without a query read row 0 (finite) and are masked
+  const int jq = qg * AQ + nl;
+  const bool qok = jq < nq;
+  const u16* qrow = q + (size_t)(b * M + (qok ? jq : 0)) * d + h * HD + 8 * g;
+  bf16x8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s] = ldfrag(qrow + 32 * s);
+  const int qpos = p0 + jq;  // the query's cache position
+
+  // Ring of two blocks.  Block i of this wave is split*bps + wv + AW*i; a load past the
+  // wave's share or the row's end re-reads the wave's last block in bounds (a cache
+  // hit) and the scores of a block outside the share are masked, so no load sits
+  // behind a branch.
+  bf16x8 kf[2][2][NS];
+  bf16x8 vf[2][NT];
+  const int blk0 = split * bps + wv;
+  auto load = [&](int slot, int i) {
+    const int blk = min(blk0 + AW * min(i, npw - 1), nblk - 1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        kf[slot][kt][s] = ldfrag(kh + ((size_t)(2 * blk + kt) * NS + s) * 512 + 8 * lane);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) vf[slot][u] = ldfrag(vh + ((size_t)blk * NT + u) * 512 + 8 * lane);
+  };
+  float m = -INFINITY, l = 0.f;  // running max / sum of query nl (replicated over g)
+  floatx4 o[NT];                 // O[query 4g + e][dim 16u + nl]
+#pragma unroll
+  for (int u = 0; u < NT; ++u) o[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot, int i) {
+    const bool in_share = i < npw;
+    const int kb = (blk0 + AW * i) * AKB;  // first key position of the block
+    float sc[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[slot][kt][s], qf[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kp = kb + 16 * kt + 4 * g + e;
+        sc[kt][e] = (in_share && qok && kp <= qpos) ? acc[e] * scale : -INFINITY;
+      }
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mb = fmaxf(mb, sc[kt][e]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);
+    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
+    float p[2][4], ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[kt][e] = (sc[kt][e] == -INFINITY) ? 0.f : expf(sc[kt][e] - mn);
+        ps += p[kt][e];
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = mn;
+    // O rows are queries 4g + e; their factors sit in lanes 4g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ae = __shfl(alpha, 4 * g + e, 64);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) o[u][e] *= ae;
+    }
+    // O += P V with P split into bf16 hi + lo parts (two MFMAs per dim tile): query nl,
+    // keys (4g + e | 16 + 4g + e) = the V key order, so P never moves between lanes;
+    // the split keeps P's value to ~16 bits, and the result matched an fp32-P evaluation
+    // to the last digit of its error statistics against an fp64 reference
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 hi8, lo8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float pv = p[t >> 2][t & 3];
+      const u16 hb = f32_to_bf16(pv);
+      hi8[t] = hb;
+      lo8[t] = f32_to_bf16(pv - bf16_to_f32(hb));
+    }
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, hi8), plo = __builtin_bit_cast(bf16x8, lo8);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf[slot][u], o[u], 0, 0, 0);
+      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf[slot][u], o[u], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // slot 0 issued first, as in the steady state
+  load(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // scheduling fences: a slot is refilled right after its use, and the next slot's use
+  // stays behind that refill (so two blocks are always in flight)
+  for (int i = 0; i < npw; i += 2) {
+    compute(0, i);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(1, i + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // wave states -> LDS; merge the 4 waves: thread -> (query jj, dims)
+  if (lane < AQ) {
+    wm[wv][lane] = m;
+    wl[wv][lane] = l;
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wo[wv][4 * g + e][16 * u + nl] = o[u][e];
+  __syncthreads();
+  constexpr int TPQ = AW * 64 / AQ;  // threads per query (16)
+  constexpr int DPT = HD / TPQ;      // dims per thread (8 or 4)
+  const int jj = threadIdx.x / TPQ, tt = threadIdx.x % TPQ;
+  const int j = qg * AQ + jj;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) mx = fmaxf(mx, wm[w][jj]);
+  float f[AW];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) {
+    f[w] = (wm[w][jj] == -INFINITY) ? 0.f : expf(wm[w][jj] - mx);
+    lsum += f[w] * wl[w][jj];
+  }
+  float v[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < AW; ++w) a += f[w] * wo[w][jj][tt * DPT + k];
+    v[k] = a;
+  }
+  if (n_active == 1) {
+    // one split: this workgroup has the whole row; padding rows of the group are zeros
+    if (j < jend) {
+      uint32_t ov[DPT / 2];
+#pragma unroll
+      for (int k = 0; k < DPT / 2; ++k)
+        ov[k] = j < nq ? (f32_to_bf16(v[2 * k] / lsum) |
+                          ((uint32_t)f32_to_bf16(v[2 * k + 1] / lsum) << 16))
+                       : 0u;
+      u16* dst = out + ((size_t)b * M + j) * d + h * HD + tt * DPT;
+      if constexpr (DPT == 8)
+        *reinterpret_cast<uint4*>(dst) = uint4{ov[0], ov[1], ov[2], ov[3]};
+      else
+        *reinterpret_cast<uint2*>(dst) = uint2{ov[0], ov[1]};
+    }
+    return;
+  }
+  // partials of (b, h): O rows [nsplit][M][HD], then (max, sum) pairs [nsplit][M][2]
+  const int Bt = gridDim.z / NG;
+  const size_t obytes = (size_t)nsplit * M * HD * 4, mlbytes = (size_t)nsplit * M * 8;
+  const float* po = part + (((size_t)b * H + h) * nsplit) * M * HD;
+  const float* pml = part + (size_t)Bt * H * nsplit * M * HD + (((size_t)b * H + h) * nsplit) * M * 2;
+  const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(po, obytes), rml = coherent_rsrc(pml, mlbytes);
+  if (j < nq) {
+    const size_t row = (size_t)split * M + j;
+#pragma unroll
+    for (int k = 0; k < DPT; k += 4)
+      __builtin_amdgcn_raw_buffer_store_b128(float4v{v[k], v[k + 1], v[k + 2], v[k + 3]}, ro,
+                                             (int)((row * HD + tt * DPT + k) * 4), 0,
+                                             kCoherentSc1);
+    if (tt == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(float2v{mx, lsum}, rml, (int)(row * 8), 0,
+                                            kCoherentSc1);
+  }
+  // count this workgroup in once its partial is written
+  const int cidx = (b * H + h) * NG + qg;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_flag = atomicAdd(&counters[cidx], 1u) == (unsigned)(n_active - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  // The last workgroup merges the splits in split order: a thread takes 4 dims of one
+  // query and issues the loads of up to SM splits at once (one memory round trip per SM
+  // splits; clamped indices, no branches around the loads).
+  constexpr int NQD = HD / 4, SM = 16;
+  for (int item = threadIdx.x; item < (jend - qg * AQ) * NQD; item += AW * 64) {
+    const int jr = qg * AQ + item / NQD, c4 = 4 * (item % NQD);
+    float r[4] = {0.f, 0.f, 0.f, 0.f};  // padding rows of this group are written as zeros
+    if (jr < nq) {
+      float mm = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < n_active; cb += SM) {
+        float2v ml[SM];
+        float4v oc[SM];
+#pragma unroll
+        for (int u = 0; u < SM; ++u) {
+          const size_t row = (size_t)min(cb + u, n_active - 1) * M + jr;
+          ml[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(row * 8), 0, kCoherentSc1);
+          oc[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)((row * HD + c4) * 4), 0,
+                                                        kCoherentSc1);
+        }
+#pragma unroll
+        for (int u = 0; u < SM; ++u) {
+          if (cb + u >= n_active || ml[u].x == -INFINITY) continue;
+          const float nm = fmaxf(mm, ml[u].x);
+          const float s0 = mm == -INFINITY ? 0.f : expf(mm - nm);
+          const float s1 = expf(ml[u].x - nm);
+          den = den * s0 + ml[u].y * s1;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) num[k] = num[k] * s0 + oc[u][k] * s1;
+          mm = nm;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = num[k] / den;
+    }
+    const uint32_t lo = f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+    const uint32_t hi = f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+    *reinterpret_cast<uint2*>(out + ((size_t)b * M + jr) * d + h * HD + c4) = uint2{lo, hi};
+  }
+  if (threadIdx.x == 0) counters[cidx] = 0u;
+}
+
+// Blocks per wave: the smallest power of two that fits the grid over the cache capacity
+// in one round of resident workgroups (two per compute unit), so no workgroup waits for
+// a second round; a wave streams its blocks through its two-block ring.
+int attn_npw(int B, int H, int M, int max_len) {
+  const long blocks = cdiv(max_len, AKB), groups = (long)B * H * cdiv(M, AQ);
+  const long resident = 2L * device_cus();
+  int npw = 1;
+  while (npw < 1024 && groups * ((blocks + AW * npw - 1) / (AW * npw)) > resident) npw <<= 1;
+  return npw;
+}
+
+int attn_nsplit(int B, int H, int M, int max_len) {
+  return cdiv(cdiv(max_len, AKB), AW * attn_npw(B, H, M, max_len));
+}
+
+int attn_groups(int M) { return cdiv(M, AQ); }
+
+hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, size_t row_stride,
+                                 size_t head_stride, int B, int M, int H, int hd,
+                                 const int32_t* pos0, const int32_t* ntok_eff, float* part,
+                                 unsigned* counters, int max_len, u16* out, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
+  const int npw = attn_npw(B, H, M, max_len);
+  const int nsplit = attn_nsplit(B, H, M, max_len);
+  const dim3 grid(nsplit, H, B * attn_groups(M));
+  if (hd == 128)
+    hipExtLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(AW * 64), 0, s, e0, e1, 0, q, M, H, kc,
+                          vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
+                          npw, out);
+  else if (hd == 64)
+    hipExtLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(AW * 64), 0, s, e0, e1, 0, q, M, H, kc,
+                          vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
+                          npw, out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ layout conversion -----
+
+// Natural [L][B][2][H][n][hd] block <-> the cache's packed head regions (positions
+// [0, n) of every row, layer and head).  One thread per element.
+__global__ void k_kv_convert(u16* __restrict__ cache, u16* __restrict__ nat, int L, int B,
+                             int H, int hd, int n, size_t layer_stride, size_t row_stride,
+                             size_t kv_stride, size_t head_stride, int to_cache) {
+  const size_t total = (size_t)L * B * 2 * H * n * hd;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    size_t r = idx;
+    const int i = (int)(r % hd); r /= hd;
+    const int p = (int)(r % n); r /= n;
+    const int hh = (int)(r % H); r /= H;
+    const int kv = (int)(r % 2); r /= 2;
+    const int bb = (int)(r % B);
+    const int ll = (int)(r / B);
+    u16* head = cache + (size_t)ll * layer_stride + (size_t)bb * row_stride +
+                (size_t)kv * kv_stride + (size_t)hh * head_stride;
+    const size_t off = kv == 0 ? kv_k_offset(p, i, hd) : kv_v_offset(p, i, hd);
+    if (to_cache)
+      head[off] = nat[idx];
+    else
+      nat[idx] = head[off];
+  }
+}
+
+hipError_t launch_kv_convert(u16* cache, u16* nat, int L, int B, int H, int hd, int n,
+                             size_t layer_stride, size_t row_stride, size_t kv_stride,
+                             size_t head_stride, int to_cache, hipStream_t s) {
+  const size_t total = (size_t)L * B * 2 * H * n * hd;
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  k_kv_convert<<<blocks, 256, 0, s>>>(cache, nat, L, B, H, hd, n, layer_stride, row_stride,
+                                      kv_stride, head_stride, to_cache);
+  return hipGetLastError();
+}
+
+}  // namespace specdec

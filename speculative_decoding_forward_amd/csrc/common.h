@@ -18,12 +18,10 @@ __device__ __forceinline__ float bf16_to_f32(u16 h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN)
+// round-to-nearest-even fp32 -> bf16 with the gfx950 conversion instruction (NaN stays
+// NaN); straight-line code, so it never splits a wave's control flow
 __device__ __forceinline__ u16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u16)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
+  return __builtin_bit_cast(u16, (__bf16)f);
 }
 
 // Activation element type of a model: bf16 (stored as u16) or fp32.
@@ -162,6 +160,18 @@ __device__ __forceinline__ void coherent_store_f64(double* p, double v) {
 }
 __device__ __forceinline__ double coherent_load_f64(const double* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Device-coherent 8/16-byte accesses through a buffer resource: cache policy sc1
+// (device scope), so data written by one workgroup is seen by a workgroup on another
+// XCD within the same kernel without an L2 write-back fence.
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+constexpr int kCoherentSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                           0x00020000);
 }
 
 // ------------------------------------------------------------------ misc -----------

@@ -159,9 +159,10 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
     if (mode == EPI_QKV_ROPE && sec < 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = min(r0 + mt * 16 + 4 * gq + e, R - 1);
+        // rows past a sequence's tokens may sit past max_len: their q is never used
+        const int pos = min(rowinfo[mt * 16 + 4 * gq + e].x, g.max_len - 1);
         const double2 c2 = *reinterpret_cast<const double2*>(g.rope_cs +
-                                                             ((size_t)r * half + i) * 2);
+                                                             ((size_t)pos * half + i) * 2);
         cs[e] = c2.x;
         sn[e] = c2.y;
       }
@@ -196,7 +197,8 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
             if (info.y & 2) {
               const int b = r / g.M;
               ((sec == 1) ? g.kc : g.vc)[(size_t)b * g.row_stride + (size_t)h * g.head_stride +
-                                         (size_t)info.x * g.hd + ii] = o;
+                                         (sec == 1 ? kv_k_offset(info.x, ii, g.hd)
+                                                   : kv_v_offset(info.x, ii, g.hd))] = o;
             }
           }
           break;
@@ -421,7 +423,7 @@ int gemm_blocks_x(const GemmArgs& g) {
 }
 
 // Compute units of the current device (queried once per device).
-static int device_cus() {
+int device_cus() {
   static int cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

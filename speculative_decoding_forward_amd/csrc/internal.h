@@ -35,6 +35,7 @@ struct spec_kv {
   void* data;        // [L][B][2][H][max_len][hd]
   int32_t* len;      // [B] caller-owned
   int32_t* base;     // [B] length before the last recorded append (in the arena tail)
+  double* rope;      // bf16 models: [max_len][hd/2][2] RoPE (cos, sin) (in the arena tail)
   size_t layer_stride, row_stride, kv_stride, head_stride;  // in elements
 };
 
@@ -64,7 +65,7 @@ struct GemmArgs {
   // QKV_ROPE
   const int32_t* pos0;
   int d, hd;
-  const double* rope_cs;  // [R][hd/2][2] (cos, sin) of each row's rotation angles
+  const double* rope_cs;  // [max_len][hd/2][2] (cos, sin) of the rotation angles by position
   uint16_t* q_out;
   uint16_t* kc;
   uint16_t* vc;
@@ -85,15 +86,31 @@ hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int 
                            int N, int K, float* C, int accumulate, const int32_t* ntok_eff,
                            int M, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float eps, float* x, void* h,
-                             const int32_t* pos0, int M, int hd, float theta, double* rope_cs,
-                             hipStream_t s);
+                             const float* g, float eps, float* x, void* h, hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                                  size_t row_stride, size_t head_stride, int B, int M, int H,
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,
                                  float* part, unsigned* counters, int max_len, uint16_t* out,
                                  hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-int attn_split();  // cache positions per attention workgroup
+int attn_nsplit(int B, int H, int M, int max_len);  // splits per (row, head, group)
+int attn_groups(int M);                               // query groups per row
+int device_cus();                                     // compute units of the device
+hipError_t launch_kv_convert(uint16_t* cache, uint16_t* nat, int L, int B, int H, int hd, int n,
+                             size_t layer_stride, size_t row_stride, size_t kv_stride,
+                             size_t head_stride, int to_cache, hipStream_t s);
+
+// Packed bf16 cache: element offsets inside one head region (see attention.hip).
+__host__ __device__ inline size_t kv_k_offset(int p, int i, int hd) {
+  return ((size_t)(p >> 4) * (hd >> 5) + (i >> 5)) * 512 + (((i & 31) >> 3) * 16 + (p & 15)) * 8 +
+         (i & 7);
+}
+__host__ __device__ inline size_t kv_v_offset(int p, int i, int hd) {
+  const int pk = p & 31;
+  const int g = (pk & 15) >> 2, e = (pk & 3) + ((pk >> 4) << 2);
+  return ((size_t)(p >> 5) * (hd >> 4) + (i >> 4)) * 512 + (g * 16 + (i & 15)) * 8 + e;
+}
+// positions a bf16 head region holds (max_len rounded up to whole 32-key blocks)
+inline int kv_capacity(int max_len) { return (max_len + 31) / 32 * 32; }
 
 // forward pieces
 hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,

@@ -68,7 +68,7 @@ def test_fp32_tiny_prefill_then_verify(name):
     assert np.all(st == 0)
     assert np.array_equal(kv.len.cpu().numpy(), oc.len)
     # cache contents of every written position
-    data = kv.data().cpu().numpy()
+    data = kv.export(max_len).cpu().numpy()
     for l in range(shape.n_layers):
         for b in range(B):
             n = oc.len[b]
@@ -99,7 +99,7 @@ def test_bf16_micro_ragged(kind, hd):
             assert err <= 1e-2      # two narrow layers: within 1e-2 outright
         assert np.all(g[b, n:] == 0)
     assert np.array_equal(kv.len.cpu().numpy(), oc.len)
-    data = kv.data().float().cpu().numpy()
+    data = kv.export(max_len).float().cpu().numpy()
     for b in range(B):
         s0, n = 150, n_tok[b]
         if n == 0:
@@ -181,7 +181,7 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
     max_len = wl.ctx + K + 1
     kv = binding.KVCache(shape, B, max_len)
     fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=seed, device=DEV)
-    kv.data().copy_(fill)
+    kv.import_(fill)
     kv.len.fill_(wl.ctx)
     new = synth.context_ids(seed + 9, B, K + 1, shape.vocab)
     g, st = gpu_forward(m, kv, new)
@@ -227,17 +227,17 @@ def test_verify_equals_single_token_calls_bitwise(wl_name, B):
     fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=0, device=DEV)
     new = synth.context_ids(9, B, K + 1, shape.vocab)
     kv1 = binding.KVCache(shape, B, max_len)
-    kv1.data().copy_(fill)
+    kv1.import_(fill)
     kv1.len.fill_(wl.ctx)
     g1, st1 = gpu_forward(m, kv1, new)
     kv2 = binding.KVCache(shape, B, max_len)
-    kv2.data().copy_(fill)
+    kv2.import_(fill)
     kv2.len.fill_(wl.ctx)
     g2 = np.concatenate([gpu_forward(m, kv2, new[:, j:j + 1])[0] for j in range(K + 1)], axis=1)
     assert np.array_equal(g1, g2)
-    assert torch.equal(kv1.data(), kv2.data())
+    assert torch.equal(kv1.export(max_len), kv2.export(max_len))
     kv3 = binding.KVCache(shape, B, max_len)
-    kv3.data().copy_(fill)
+    kv3.import_(fill)
     kv3.len.fill_(wl.ctx)
     g3, _ = gpu_forward(m, kv3, new)
     assert np.array_equal(g1, g3)
@@ -248,3 +248,23 @@ def test_verify_equals_single_token_calls_bitwise(wl_name, B):
     g4, _ = gpu_forward(m, kv3, alt)
     assert np.array_equal(g1[:, :K], g4[:, :K])
     assert not np.array_equal(g1[:, K], g4[:, K])
+
+
+@pytest.mark.parametrize("dtype,hd,max_len", [("bf16", 128, 100), ("bf16", 64, 64), ("f32", 32, 40)])
+def test_kv_import_export_roundtrip(dtype, hd, max_len):
+    """Natural-order positions written with spec_kv_import read back unchanged with
+    spec_kv_export (bf16 caches store them in the attention's packed order), and
+    positions past the imported range are left alone."""
+    shape = synth.ModelShape(n_layers=2, d_model=2 * hd, n_heads=2, head_dim=hd, d_ffn=256,
+                             vocab=64, ffn_kind="gelu", dtype=dtype)
+    B = 3
+    kv = binding.KVCache(shape, B, max_len)
+    full = synth.kv_fill(shape, B, max_len, max_len, seed=5, device=DEV)
+    kv.import_(full)
+    assert torch.equal(kv.export(max_len), full)
+    part = synth.kv_fill(shape, B, max_len, max_len, seed=6, device=DEV)
+    n = max_len // 2 + 1
+    kv.import_(part[:, :, :, :, :n].contiguous())
+    got = kv.export(max_len)
+    assert torch.equal(got[:, :, :, :, :n], part[:, :, :, :, :n])
+    assert torch.equal(got[:, :, :, :, n:], full[:, :, :, :, n:])
