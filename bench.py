@@ -43,16 +43,22 @@ def parse():
 
 def gemm_bytes_per_verify(shape, R):
     """Algorithmic bytes of the weight GEMMs of one forward over R rows: every weight
-    once, the activation rows read, the fp32 outputs written (read too when added)."""
+    once and the activation rows read; outputs: q / K / V / FFN activations in the
+    element type (QKV, up), the residual rows read and written in fp32 plus the next
+    product's input and its per-16-column sums of squares (O-proj, down), fp32 logits
+    (LM head).  Normalised products also read their rows' sums of squares."""
     d, F, V, L = shape.d_model, shape.d_ffn, shape.vocab, shape.n_layers
     e = shape.elt_bytes()
     ffn_in = 2 * F if shape.ffn_kind == "swiglu" else F
-    gemms = [(3 * d, d, 0), (d, d, 1), (ffn_in, d, 0), (d, F, 1)]  # (N, K, accumulate)
+    ss = R * (d // 16) * 4
+    resid_out = R * d * 4 * 2 + R * d * e + ss
+    gemms = [(3 * d, d, R * 3 * d * e + ss), (d, d, resid_out), (ffn_in, d, R * F * e + ss),
+             (d, F, resid_out)]  # (N, K, output-side bytes)
     total, n = 0, 0
-    for N, K, acc in gemms:
-        total += L * (N * K * e + R * K * e + R * N * 4 * (2 if acc else 1))
+    for N, K, out in gemms:
+        total += L * (N * K * e + R * K * e + out)
         n += L
-    total += V * d * e + R * d * e + R * V * 4
+    total += V * d * e + R * d * e + ss + R * V * 4
     n += 1
     return total, n
 

@@ -17,17 +17,21 @@ in tests/test_oracle_model.py.
 Layer spec (pre-norm decoder, no biases, untied embedding and LM head):
   x = E[tok]                                     residual stream (float64 here)
   per layer:
-    h = bf16(RMSNorm(x) * g1)                    RMSNorm(x) = x / sqrt(mean(x^2) + eps)
-    q, k, v = h W_qkv^T                          W_qkv rows: [q heads | k heads | v heads]
+    q, k, v = N(x, g1) W_qkv^T                   W_qkv rows: [q heads | k heads | v heads]
     RoPE on q, k at absolute position (half-split pairs (i, i + hd/2),
        angle = pos * theta^(-2i/hd))
     q, k, v = bf16(.); k, v appended to the cache
     o = bf16(softmax(q K^T / sqrt(hd), causal) V)
     x += o W_o^T
-    h = bf16(RMSNorm(x) * g2)
-    GELU:   a = bf16(gelu(h W1^T)),           x += a W2^T       gelu(t) = t * Phi(t)
-    SwiGLU: a = bf16(silu(h Wg^T) * (h Wu^T)), x += a Wd^T       silu(t) = t / (1 + e^-t)
-  logits = bf16(RMSNorm(x) * g_f) W_head^T
+    GELU:   a = bf16(gelu(N(x, g2) W1^T)),                  x += a W2^T
+    SwiGLU: a = bf16(silu(N(x, g2) Wg^T) * (N(x, g2) Wu^T)), x += a Wd^T
+  logits = N(x, g_f) W_head^T
+with the RMS-normalised product
+    N(x, g) W^T = s(x) * (bf16(x * g) W^T),   s(x) = 1 / sqrt(mean(x^2) + eps)
+per row: RMSNorm(x) * g = s(x) * (x * g), and the row factor s(x) is taken out of the
+product, so the matrix input is rounded to bf16 before normalisation and the fp32
+product row is scaled after it (the same quantity as bf16(RMSNorm(x) * g) W^T up to
+where the one bf16 rounding falls).  gelu(t) = t * Phi(t), silu(t) = t / (1 + e^-t).
 For float32 models every bf16() is the identity.  Arithmetic is float64 throughout;
 bf16() rounds the float64 value to nearest-even bf16 directly.
 
@@ -79,6 +83,19 @@ def rmsnorm(x, g, eps):
     x = np.asarray(x, dtype=np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rms_scale(x, eps):
+    """s(x) = 1 / sqrt(mean(x^2) + eps) per row (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def normed_matmul(x, g, w, eps, rb):
+    """N(x, g) W^T = s(x) * (rb(x * g) W^T): RMSNorm with gain g, its row factor taken
+    out of the product (see the layer spec above)."""
+    x = np.asarray(x, dtype=np.float64)
+    return rms_scale(x, eps) * matmul(rb(x * np.asarray(g, dtype=np.float64)), w)
 
 
 def rope(t, pos, theta):
@@ -195,8 +212,7 @@ def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
             w1, w2 = f64(f"l{l}.w1"), f64(f"l{l}.w2")
         for b in rows:
             n, s0, p = int(n_tok[b]), L0[b], pos[b]
-            h = rb(rmsnorm(x[b], g1, c.norm_eps))
-            qkv = matmul(h, wqkv)
+            qkv = normed_matmul(x[b], g1, wqkv, c.norm_eps, rb)
             q = qkv[:, :d].reshape(n, H, hd)
             k = qkv[:, d:2 * d].reshape(n, H, hd)
             v = qkv[:, 2 * d:].reshape(n, H, hd)
@@ -208,17 +224,18 @@ def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
             o = attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], p)
             o = o.reshape(n, d)
             xb = x[b] + matmul(rb(o), wo)
-            h = rb(rmsnorm(xb, g2, c.norm_eps))
             if c.ffn_kind == "swiglu":
-                a = rb(silu(matmul(h, wg)) * matmul(h, wu))
+                gate = normed_matmul(xb, g2, wg, c.norm_eps, rb)
+                up = normed_matmul(xb, g2, wu, c.norm_eps, rb)
+                a = rb(silu(gate) * up)
                 xb = xb + matmul(a, wd)
             else:
-                a = rb(gelu(matmul(h, w1)))
+                a = rb(gelu(normed_matmul(xb, g2, w1, c.norm_eps, rb)))
                 xb = xb + matmul(a, w2)
             x[b] = xb
     logits = np.zeros((B, M, c.vocab))
     head, gf = f64("head"), f64("norm_f")
     for b in rows:
-        logits[b, :n_tok[b]] = matmul(rb(rmsnorm(x[b], gf, c.norm_eps)), head)
+        logits[b, :n_tok[b]] = normed_matmul(x[b], gf, head, c.norm_eps, rb)
     cache.len = cache.len + n_tok
     return logits

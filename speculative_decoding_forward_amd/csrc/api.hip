@@ -103,7 +103,9 @@ struct FwdWS {
   void* q;            // rotated queries [R, d]
   void* att;          // attention output [R, d]
   float* part;        // attention partials
-  float* ypart;       // residual GEMMs: Y [R, d] before it is added to x
+  float* ss;          // bf16: partial sums of x^2 per row and 16-column group [R, d/16]
+  float* rowscale;    // fp32 models: RMS row factor of the normalised input [R]
+  double* rope_rows;  // bf16: (cos, sin) of each row's RoPE angles [R, hd/2, 2]
   float* logits;      // draft-step logits [R, V]
   size_t total;
 };
@@ -141,7 +143,9 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
                             ? (size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4
                             : 0);
   w.logits = (float*)take(R * V * 4);
-  w.ypart = (float*)take(c.dtype == SPEC_DT_BF16 ? (size_t)R * d * 4 : 0);
+  w.ss = (float*)take(c.dtype == SPEC_DT_BF16 ? R * (d / 16) * 4 : 0);
+  w.rowscale = (float*)take(c.dtype == SPEC_DT_F32 ? R * 4 : 0);
+  w.rope_rows = (double*)take(c.dtype == SPEC_DT_BF16 ? R * c.head_dim * 8 : 0);
   w.total = off;
   return w;
 }
@@ -194,10 +198,10 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
     const spec_model::Layer& L = m->layers[l];
     char* kl = (char*)kv->data + (size_t)l * kv->layer_stride * e;
     char* vl = kl + kv->kv_stride * e;
-    SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm1, R, d, c.norm_eps, dt, w.h, s));
+    SPEC_LAUNCH(launch_norm_input(w.x, L.norm1, R, d, c.norm_eps, (float*)w.h, w.rowscale, s));
     Ev e1 = timed(g_timing.gemm);
     SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.wqkv, nullptr, 3 * d, R,
-                                3 * d, d, w.y, 0, nullptr, M, s, e1.e0, e1.e1));
+                                3 * d, d, w.y, 0, w.rowscale, nullptr, M, s, e1.e0, e1.e1));
     SPEC_LAUNCH(launch_rope_append(dt, w.y, B, M, H, hd, c.rope_theta, w.pos0, w.ntok_eff, w.q,
                                    kl, vl, kv->row_stride, kv->head_stride, kv->max_len, s));
     Ev e2 = timed(g_timing.attn);
@@ -206,32 +210,33 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
                                      w.ntok_eff, kv->max_len, (float*)w.att, s, e2.e0, e2.e1));
     Ev e3 = timed(g_timing.gemm);
     SPEC_LAUNCH(launch_gemm_f32((const float*)w.att, (const float*)L.wo, nullptr, d, R, d, d,
-                                w.x, 1, nullptr, M, s, e3.e0, e3.e1));
-    SPEC_LAUNCH(launch_rmsnorm(w.x, L.norm2, R, d, c.norm_eps, dt, w.h, s));
+                                w.x, 1, nullptr, nullptr, M, s, e3.e0, e3.e1));
+    SPEC_LAUNCH(launch_norm_input(w.x, L.norm2, R, d, c.norm_eps, (float*)w.h, w.rowscale, s));
     Ev e4 = timed(g_timing.gemm);
     if (swiglu)
       SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.w_up,
-                                  (const float*)L.w_up2, F, R, 2 * F, d, w.y, 0, nullptr, M, s,
-                                  e4.e0, e4.e1));
+                                  (const float*)L.w_up2, F, R, 2 * F, d, w.y, 0, w.rowscale,
+                                  nullptr, M, s, e4.e0, e4.e1));
     else
       SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.w_up, nullptr, F, R, F, d,
-                                  w.y, 0, nullptr, M, s, e4.e0, e4.e1));
+                                  w.y, 0, w.rowscale, nullptr, M, s, e4.e0, e4.e1));
     SPEC_LAUNCH(launch_act(dt, c.ffn_kind, w.y, R, F, w.a, s));
     Ev e5 = timed(g_timing.gemm);
     SPEC_LAUNCH(launch_gemm_f32((const float*)w.a, (const float*)L.w_down, nullptr, d, R, d, F,
-                                w.x, 1, nullptr, M, s, e5.e0, e5.e1));
+                                w.x, 1, nullptr, nullptr, M, s, e5.e0, e5.e1));
   }
-  SPEC_LAUNCH(launch_rmsnorm(w.x, m->norm_f, R, d, c.norm_eps, dt, w.h, s));
+  SPEC_LAUNCH(launch_norm_input(w.x, m->norm_f, R, d, c.norm_eps, (float*)w.h, w.rowscale, s));
   Ev e6 = timed(g_timing.gemm);
   SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)m->head, nullptr, V, R, V, d,
-                              logits, 0, w.ntok_eff, M, s, e6.e0, e6.e1));
+                              logits, 0, w.rowscale, w.ntok_eff, M, s, e6.e0, e6.e1));
   return SPEC_OK;
 }
 
-// bf16 models: 7 kernels per layer.
-//   QKV GEMM (+ RoPE, q out, K/V append) -> attention (+ split merge) ->
-//   O GEMM (K-split partials) -> residual add + row norm -> up GEMM (+ SwiGLU / GELU)
-//   -> down GEMM (K-split partials) -> residual add + row norm (next layer's / final)
+// bf16 models: 5 kernels per layer.
+//   QKV GEMM (row factor, RoPE, q out, K/V append) -> attention (+ split merge) ->
+//   O GEMM (x += y, next input bf16(x * g2) and its sums of squares) ->
+//   up GEMM (row factor, SwiGLU / GELU) -> down GEMM (x += y, next input and sums of
+//   squares for the next layer's QKV or the LM head)
 spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
                          const FwdWS& w, hipStream_t s) {
   const spec_model_cfg& c = m->cfg;
@@ -239,8 +244,8 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
-  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, c.norm_eps, w.x,
-                                w.h, s));
+  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.h, w.ss,
+                                kv->rope, w.pos0, M, hd, kv->max_len, w.rope_rows, s));
   GemmArgs base{};
   base.R = R;
   base.M = M;
@@ -248,11 +253,13 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.pos0 = w.pos0;
   base.d = d;
   base.hd = hd;
-  base.rope_cs = kv->rope;
+  base.rope_rows = w.rope_rows;
   base.row_stride = kv->row_stride;
   base.head_stride = kv->head_stride;
   base.max_len = kv->max_len;
   base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
+  base.ss_np = d / 16;
+  base.eps = c.norm_eps;
   for (int l = 0; l < c.n_layers; ++l) {
     const spec_model::Layer& L = m->layers[l];
     uint16_t* kl = (uint16_t*)((char*)kv->data + (size_t)l * kv->layer_stride * e);
@@ -268,6 +275,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.q_out = (uint16_t*)w.q;
       g.kc = kl;
       g.vc = vl;
+      g.ss_in = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
@@ -286,12 +294,12 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.W = (const uint16_t*)L.wo;
       g.N = g.N1 = d;
       g.K = d;
-      g.C = w.ypart;
-      g.ldc = d;
+      g.x = w.x;
+      g.gain = L.norm2;
+      g.h_out = (uint16_t*)w.h;
+      g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
-      SPEC_LAUNCH(launch_resid_norm(w.x, w.ypart, R, d, L.norm2, c.norm_eps,
-                                    (uint16_t*)w.h, s));
     }
     {
       GemmArgs g = base;
@@ -299,6 +307,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.lda = d;
       g.K = d;
       g.act_out = (uint16_t*)w.a;
+      g.ss_in = w.ss;
       g.W = (const uint16_t*)L.w_up;
       if (c.ffn_kind == SPEC_FFN_SWIGLU) {
         g.mode = EPI_SWIGLU;
@@ -319,13 +328,12 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.W = (const uint16_t*)L.w_down;
       g.N = g.N1 = d;
       g.K = F;
-      g.C = w.ypart;
-      g.ldc = d;
+      g.x = w.x;
+      g.gain = l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f;
+      g.h_out = (uint16_t*)w.h;
+      g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
-      SPEC_LAUNCH(launch_resid_norm(w.x, w.ypart, R, d,
-                                    l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f,
-                                    c.norm_eps, (uint16_t*)w.h, s));
     }
   }
   GemmArgs g = base;
@@ -335,6 +343,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   g.W = (const uint16_t*)m->head;
   g.N = g.N1 = V;
   g.K = d;
+  g.ss_in = w.ss;
   g.C = logits;
   g.ldc = V;
   Ev ev = timed(g_timing.gemm);

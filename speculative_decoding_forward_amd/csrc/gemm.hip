@@ -25,9 +25,14 @@
 //              the KV cache at the row's position
 //   SWIGLU     columns paired (gate n, up n): a = bf16(silu(g) * u)
 //   GELU       a = bf16(gelu(y)), erf form
-//   RESID      partial Y of the workgroup's K split -> fp32 buffer; k_resid_norm then
-//              adds the splits to the residual stream x in split order and forms
-//              h = bf16(RMSNorm(x) * g), the next matrix's input
+//   RESID      x += Y on the residual stream (each column belongs to one tile, so the
+//              update is race-free), h = bf16(x * g) for the next normalised product and
+//              the tile's partial sums of x^2 per row (16 columns each, summed in
+//              fp64, stored as fp32)
+// A normalised product (QKV_ROPE, SWIGLU, GELU, STORE) takes A = bf16(x * g) and
+// scales output row r by s_r = 1 / sqrt(mean(x_r^2) + eps), summed from those
+// partials in a fixed order: RMSNorm(x) * g = s * (x * g), with the row factor taken
+// out of the product, so no separate normalisation pass is needed.
 //
 // fp32 path (small fp32 models): separate simple kernels, one wave per output column.
 #include <hip/hip_ext.h>
@@ -65,6 +70,16 @@ __device__ __forceinline__ bf16x8 ld8_nt(const u16* p, bool ok) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Exact quotient a / b for 0 <= a < 2^22, 1 <= b < 2^12 from a float reciprocal plus one
+// correction step each way (a few instructions instead of the ~25 of an integer
+// division), for index math on the epilogue wave's path to its first memory requests.
+__device__ __forceinline__ int qdiv(int a, int b) {
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  q -= (q * b > a) ? 1 : 0;
+  q += ((q + 1) * b <= a) ? 1 : 0;
+  return q;
+}
+
 // Packed weight layout.  A matrix is stored as a sequence of column tiles, each the
 // 16 weight rows behind 16 output columns; tile t, super-step j (k in [128j, 128j+128)),
 // MFMA slice s (k in [128j + 32s, +32)) and lane l hold, contiguously,
@@ -83,9 +98,9 @@ struct QkvTile {
 __device__ __forceinline__ QkvTile qkv_tile(int t, int d, int hd) {
   const int half = hd >> 1, per_head = half / 8, per_sec = d / 16;
   QkvTile q;
-  q.sec = t / per_sec;
+  q.sec = qdiv(t, per_sec);
   const int rem = t - q.sec * per_sec;
-  q.h = rem / per_head;
+  q.h = qdiv(rem, per_head);
   q.i0 = 8 * (rem - q.h * per_head);
   return q;
 }
@@ -133,93 +148,225 @@ hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd,
   return hipGetLastError();
 }
 
+// LDS the epilogue wave stages its inputs in.  With one row tile (MT = 1) every input
+// of the epilogue comes from LDS, copied there by direct global-to-LDS loads that the
+// epilogue wave issues first thing, so they are in flight early and need no registers
+// (once the weight stream saturates HBM a load waits several microseconds, and an
+// epilogue waiting for one would hold the streaming waves at the next tile barrier):
+// the row factors' partial sums, the RoPE factors of the block's rows and, for RESID,
+// the residual values and norm gains of the current tile.  With more row tiles only the
+// partial sums are staged (16 rows at a time) and the other inputs are read from global
+// memory.
+constexpr int SS_NP_MAX = 512;     // partial sums per row (d_model <= 8192)
+constexpr int ROPE_HALF_MAX = 64;  // rotation pairs per head (head_dim <= 128)
+
+// Dynamic LDS of the epilogue wave, sized per launch (epi_lds_bytes): partial sums of up
+// to 16 rows, RoPE factors of the block's rows (one row tile, QKV_ROPE), and the
+// residual values and gains of one tile (RESID).
+struct EpiLds {
+  float* ss;       // [min(16, rows)][np]
+  double2* rope;   // [rows][hd/2]
+  float* xres;     // [16][16]
+  float* gain;     // [16]
+};
+
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ inline int epi_lds_bytes(int mt, int mode, int rows16, int np, int half,
+                                             int rows, bool norm_in) {
+  int b = norm_in ? align16(rows16 * np * 4) : 0;
+  if (mt == 1 && mode == EPI_QKV_ROPE) b += align16(rows * half * 16);
+  return b + 16 * 16 * 4 + 16 * 4;
+}
+
+// Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` with direct loads: lane l
+// of pass k moves bytes [1024 k + 16 l, +16).
+__device__ __forceinline__ void lds_copy(const void* src, void* dst, int bytes, int lane) {
+  for (int off = 0; off < bytes; off += 1024) {
+    if (off + 16 * lane < bytes)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)((const char*)src + off + 16 * lane),
+          (__attribute__((address_space(3))) void*)((char*)dst + off), 16, 0, 0);
+  }
+}
+
+// Residual values x[r0 + row][16 t .. 16 t + 15] (rows < rows) and gains of tile t.
+__device__ __forceinline__ void lds_copy_resid(const GemmArgs& g, int t, int r0, int rows,
+                                               float* xres, float* gain, int lane) {
+  const int row = lane >> 2, q = lane & 3;
+  if (row < rows)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(g.x + (size_t)(r0 + row) * g.N + 16 * t +
+                                                        4 * q),
+        (__attribute__((address_space(3))) void*)xres, 16, 0, 0);
+  if (lane < 4)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(g.gain + 16 * t + 4 * lane),
+        (__attribute__((address_space(3))) void*)gain, 16, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads, direct-to-LDS ones included.
+__device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Row factors s_r = 1 / sqrt(sum_p ss[r][p] / K + eps) of `rows` (<= 16) rows whose np
+// partial sums sit in LDS: four lanes per row add contiguous quarters in column order
+// (fp64) and combine them by a fixed butterfly, the same order for every row count.
+__device__ __forceinline__ void row_factors(const float* ss, int rows, int np, int K, float eps,
+                                            int lane, double* rowscale) {
+  const int row = lane >> 2, qq = lane & 3, per = np >> 2;  // np is a multiple of 8
+  double part = 0.0;
+  if (row < rows) {
+    const float4* src = reinterpret_cast<const float4*>(ss + row * np + qq * per);
+    for (int c = 0; c < (per >> 2); ++c) {
+      const float4 v = src[c];
+      part += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+    }
+    if (per & 3)
+      for (int c = per & ~3; c < per; ++c) part += (double)ss[row * np + qq * per + c];
+  }
+  part += __shfl_xor(part, 1, 64);
+  part += __shfl_xor(part, 2, 64);
+  if (qq == 0 && row < rows) rowscale[row] = 1.0 / sqrt(part / K + (double)eps);
+}
+
+template <int MT>
+__device__ __forceinline__ floatx4 sum_partials(const floatx4 (*part)[MT][64], int mt, int lane) {
+  floatx4 v = part[0][mt][lane];
+#pragma unroll
+  for (int w = 1; w < GW; ++w) {
+    const floatx4 p = part[w][mt][lane];
+    v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+  }
+  return v;
+}
+
 // Per-tile epilogue, run by the workgroup's epilogue wave.  part[w][mt][lane] holds
 // wave w's MFMA accumulator fragment of row tile mt: lane l has rows 4(l/16)+e
 // (e = 0..3) of local column l%16.  The GW partials are summed in wave order.
 // rowinfo[rr] = (absolute position, flags) of row r0 + rr: flag 1 = a real token of its
 // sequence, flag 2 = its K/V may be written (real token and position < max_len).
+// One loop per mode, so each mode's registers are allocated on its own.
 template <int MT>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int r0,
                                                    const floatx4 (*part)[MT][64],
-                                                   const int2* rowinfo, int lane) {
+                                                   const int2* rowinfo, const double* rowscale,
+                                                   const EpiLds& L, int lane) {
   const int nl = lane & 15, gq = lane >> 4, R = g.R, mode = g.mode;
   const bool is_hi = nl >= 8;
-  int sec = 0, h = 0, i = 0;
-  const int half = g.hd >> 1;
-  if (mode == EPI_QKV_ROPE) {
-    const QkvTile qt = qkv_tile(t, g.d, g.hd);
-    sec = qt.sec;
-    h = qt.h;
-    i = qt.i0 + (nl & 7);
-  }
+  if (mode == EPI_RESID) {
+    // residual update, next input bf16(x * g) and the tile's sums of squares per row
+    const int col = 16 * t + nl, np = g.N >> 4;
+    const float gc = MT == 1 ? L.gain[nl] : g.gain[col];
 #pragma unroll 1
-  for (int mt = 0; mt < MT; ++mt) {
-    // rotation factors of this lane's four rows, loaded together (one latency)
-    double cs[4], sn[4];
-    if (mode == EPI_QKV_ROPE && sec < 2) {
+    for (int mt = 0; mt < MT; ++mt) {
+      const floatx4 v = sum_partials<MT>(part, mt, lane);
+      double sq[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // rows past a sequence's tokens may sit past max_len: their q is never used
-        const int pos = min(rowinfo[mt * 16 + 4 * gq + e].x, g.max_len - 1);
-        const double2 c2 = *reinterpret_cast<const double2*>(g.rope_cs +
-                                                             ((size_t)pos * half + i) * 2);
-        cs[e] = c2.x;
-        sn[e] = c2.y;
+        const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
+        float xn = 0.f;
+        if (r < R) {
+          const float xo = MT == 1 ? L.xres[rr * 16 + nl] : g.x[(size_t)r * g.N + col];
+          xn = xo + v[e];
+          g.x[(size_t)r * g.N + col] = xn;
+          g.h_out[(size_t)r * g.N + col] = f32_to_bf16(xn * gc);
+        }
+        sq[e] = (double)xn * xn;
+      }
+      // sum over the 16 columns of the tile (the 16 lanes of this row group), fixed order
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sq[e] += __shfl_xor(sq[e], o, 64);
+      if (nl == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + mt * 16 + 4 * gq + e;
+          if (r < R) g.ss_out[(size_t)r * np + t] = (float)sq[e];
+        }
       }
     }
-    floatx4 v = part[0][mt][lane];
+    return;
+  }
+  // normalised products: the row factor first
+#pragma unroll 1
+  for (int mt = 0; mt < MT; ++mt) {
+    floatx4 v = sum_partials<MT>(part, mt, lane);
+    if (g.ss_in) {
 #pragma unroll
-    for (int w = 1; w < GW; ++w) {
-      const floatx4 p = part[w][mt][lane];
-      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+      for (int e = 0; e < 4; ++e) v[e] = (float)((double)v[e] * rowscale[mt * 16 + 4 * gq + e]);
     }
+    if (mode == EPI_QKV_ROPE) {
+      const QkvTile qt = qkv_tile(t, g.d, g.hd);
+      const int half = g.hd >> 1, i = qt.i0 + (nl & 7), ii = is_hi ? i + half : i;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
-      const float y = v[e];
-      const float yp = __shfl_xor(y, 8);  // the paired column c ^ 8 of the same row
-      if (r >= R) continue;
-      switch (mode) {
-        case EPI_QKV_ROPE: {
+      for (int e = 0; e < 4; ++e) {
+        const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
+        const float y = v[e];
+        const float yp = __shfl_xor(y, 8);  // the paired column c ^ 8 of the same row
+        if (r >= R) continue;
+        u16 o;
+        if (qt.sec < 2) {
+          // rotation of the pair (i, i + hd/2) at the row's position, in fp64
+          double2 c2;
+          if constexpr (MT == 1) {
+            c2 = L.rope[rr * half + i];
+          } else {
+            c2 = *reinterpret_cast<const double2*>(g.rope_rows + ((size_t)r * half + i) * 2);
+          }
           const float lo = is_hi ? yp : y, hi = is_hi ? y : yp;
-          u16 o;
-          if (sec < 2) {
-            o = is_hi ? f32_to_bf16((float)((double)hi * cs[e] + (double)lo * sn[e]))
-                      : f32_to_bf16((float)((double)lo * cs[e] - (double)hi * sn[e]));
-          } else {
-            o = f32_to_bf16(y);
-          }
-          const int ii = is_hi ? i + half : i;
-          if (sec == 0) {
-            g.q_out[(size_t)r * g.d + h * g.hd + ii] = o;
-          } else {
-            const int2 info = rowinfo[rr];
-            if (info.y & 2) {
-              const int b = r / g.M;
-              ((sec == 1) ? g.kc : g.vc)[(size_t)b * g.row_stride + (size_t)h * g.head_stride +
-                                         (sec == 1 ? kv_k_offset(info.x, ii, g.hd)
-                                                   : kv_v_offset(info.x, ii, g.hd))] = o;
-            }
-          }
-          break;
+          o = is_hi ? f32_to_bf16((float)((double)hi * c2.x + (double)lo * c2.y))
+                    : f32_to_bf16((float)((double)lo * c2.x - (double)hi * c2.y));
+        } else {
+          o = f32_to_bf16(y);
         }
-        case EPI_SWIGLU:
-          if (!is_hi)
-            g.act_out[(size_t)r * g.N1 + 8 * t + nl] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
-          break;
-        case EPI_GELU:
+        if (qt.sec == 0) {
+          g.q_out[(size_t)r * g.d + qt.h * g.hd + ii] = o;
+        } else {
+          const int2 info = rowinfo[rr];
+          if (info.y & 2) {
+            const int b = r / g.M;
+            ((qt.sec == 1) ? g.kc : g.vc)[(size_t)b * g.row_stride + (size_t)qt.h * g.head_stride +
+                                          (qt.sec == 1 ? kv_k_offset(info.x, ii, g.hd)
+                                                       : kv_v_offset(info.x, ii, g.hd))] = o;
+          }
+        }
+      }
+    } else if (mode == EPI_SWIGLU) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + mt * 16 + 4 * gq + e;
+        const float y = v[e];
+        const float yp = __shfl_xor(y, 8);  // the up column paired with gate column nl
+        if (r < R && !is_hi)
+          g.act_out[(size_t)r * g.N1 + 8 * t + nl] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
+      }
+    } else if (mode == EPI_GELU) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + mt * 16 + 4 * gq + e;
+        if (r < R)
           g.act_out[(size_t)r * g.N + 16 * t + nl] =
-              f32_to_bf16(0.5f * y * (1.f + erff(y * 0.70710678118654752f)));
-          break;
-        case EPI_STORE:
-          g.C[(size_t)r * g.ldc + 16 * t + nl] = (rowinfo[rr].y & 1) ? y : 0.f;
-          break;
-        default:  // EPI_RESID: Y -> C; the row-norm kernel adds it to x
-          g.C[(size_t)r * g.ldc + 16 * t + nl] = y;
-          break;
+              f32_to_bf16(0.5f * v[e] * (1.f + erff(v[e] * 0.70710678118654752f)));
+      }
+    } else {  // EPI_STORE
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
+        if (r < R) g.C[(size_t)r * g.ldc + 16 * t + nl] = (rowinfo[rr].y & 1) ? v[e] : 0.f;
       }
     }
   }
+}
+
+// The epilogue wave's side of the per-tile barrier.  It shares only LDS with the
+// streaming waves, so it waits for its own LDS accesses and nothing else: its global
+// stores and the loads it has issued for the next tile stay in flight across the
+// barrier (__syncthreads would also wait for those).
+__device__ __forceinline__ void epi_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 // Persistent weight-streaming GEMM.  Workgroup (bx, by) owns row block by (MT*16 rows
@@ -229,34 +376,84 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
 // stream over (tile, step) and its register ring of P steps runs across tile
 // boundaries.  At the end of a tile each streaming wave parks its accumulator in LDS
 // (double-buffered by tile parity) and meets the others at one barrier; the epilogue
-// wave then sums the partials and runs the epilogue (with its own global loads and
-// stores) while the streaming waves go on with the next tile.  A streaming wave thus
-// never waits on anything but its own weight loads.
+// wave then sums the partials and runs the epilogue while the streaming waves go on with
+// the next tile.
+// Register budget: two workgroups of GW + 1 waves per CU put two waves of each on one
+// SIMD, so the kernel must fit four waves per SIMD (<= 128 VGPRs) for the grid to be
+// resident at once; the larger row tiles accept one workgroup per CU.
 template <int MT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   constexpr int P = MT <= 2 ? SPEC_GEMM_RING : (SPEC_GEMM_RING > 2 ? 2 : SPEC_GEMM_RING);
   __shared__ floatx4 part[2][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
+  __shared__ double rowscale[MT * 16];
+  extern __shared__ float4 epi_dyn[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bx = blockIdx.x, G = gridDim.x;
   const int r0 = blockIdx.y * (MT * 16);
   const int nt = (g.ntiles - bx + G - 1) / G;  // tiles of this workgroup (>= 1)
   if (wv == GW) {
-    for (int rr = lane; rr < MT * 16; rr += 64) {
-      const int r = r0 + rr;
+    const int rows = min(MT * 16, g.R - r0);  // >= 1
+    const int np = g.ss_np, half = g.hd >> 1;
+    EpiLds L;
+    {
+      char* p = reinterpret_cast<char*>(epi_dyn);
+      L.ss = reinterpret_cast<float*>(p);
+      if (g.ss_in) p += align16(min(16, g.R) * np * 4);
+      L.rope = reinterpret_cast<double2*>(p);
+      if (MT == 1 && g.mode == EPI_QKV_ROPE) p += align16(g.R * half * 16);
+      L.xres = reinterpret_cast<float*>(p);
+      L.gain = L.xres + 256;
+    }
+    // requests first: direct-to-LDS copies of the row factors' partial sums and the
+    // first tile's inputs, then the row bookkeeping
+    if (g.ss_in) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, min(16, rows) * np * 4, lane);
+    if constexpr (MT == 1) {
+      if (g.mode == EPI_QKV_ROPE)
+        lds_copy(g.rope_rows + (size_t)r0 * half * 2, L.rope, rows * half * 16, lane);
+      else if (g.mode == EPI_RESID)
+        lds_copy_resid(g, bx, r0, rows, L.xres, L.gain, lane);
+    }
+    int ntok[(MT * 16 + 63) / 64], p0v[(MT * 16 + 63) / 64];
+#pragma unroll
+    for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
+      const int r = min(r0 + lane + 64 * k, g.R - 1), b = qdiv(r, g.M);
+      ntok[k] = g.ntok_eff ? g.ntok_eff[b] : g.M;
+      p0v[k] = g.pos0 ? g.pos0[b] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
+      const int rr = lane + 64 * k, r = r0 + rr;
       int2 info{0, 0};
       if (r < g.R) {
-        const int b = r / g.M, j = r - b * g.M;
-        const int n = g.ntok_eff ? g.ntok_eff[b] : g.M;
-        const int pos = (g.pos0 ? g.pos0[b] : 0) + j;
-        info = int2{pos, (j < n ? 1 : 0) | (j < n && pos < g.max_len ? 2 : 0)};
+        const int j = r - qdiv(r, g.M) * g.M, pos = p0v[k] + j;
+        info = int2{pos, (j < ntok[k] ? 1 : 0) | (j < ntok[k] && pos < g.max_len ? 2 : 0)};
       }
-      rowinfo[rr] = info;
+      if (rr < MT * 16) rowinfo[rr] = info;
+    }
+    wait_vm();
+    if (g.ss_in) {
+      for (int rb = 0; rb < MT && 16 * rb < rows; ++rb) {
+        if (rb > 0) {  // later 16-row batches (MT > 1)
+          wave_lds_sync();
+          lds_copy(g.ss_in + (size_t)(r0 + 16 * rb) * np, L.ss, min(16, rows - 16 * rb) * np * 4,
+                   lane);
+          wait_vm();
+        }
+        row_factors(L.ss, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
+      }
     }
     wave_lds_sync();
     for (int ct = 0; ct < nt; ++ct) {
-      __syncthreads();
-      gemm_tile_epilogue<MT>(g, bx + ct * G, r0, part[ct & 1], rowinfo, lane);
+      epi_barrier();
+      gemm_tile_epilogue<MT>(g, bx + ct * G, r0, part[ct & 1], rowinfo, rowscale, L, lane);
+      if constexpr (MT == 1) {
+        if (g.mode == EPI_RESID && ct + 1 < nt) {
+          wave_lds_sync();
+          lds_copy_resid(g, bx + (ct + 1) * G, r0, rows, L.xres, L.gain, lane);
+          wait_vm();
+        }
+      }
     }
     return;
   }
@@ -340,53 +537,14 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   }
 }
 
-// Residual update and RMSNorm of the next matrix's input, one 256-thread block per row:
-//   x[r] += y[r];  h[r] = bf16(x[r] * g / rms(x[r]))
-// with the sum of squares and the scaling in fp64.
-__global__ __launch_bounds__(256) void k_resid_norm(float* __restrict__ x,
-                                                    const float* __restrict__ y, int R, int d,
-                                                    const float* __restrict__ gain, float eps,
-                                                    u16* __restrict__ h) {
-  __shared__ double red[4];
-  const int r = blockIdx.x;
-  float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
-  const float4* yr = reinterpret_cast<const float4*>(y + (size_t)r * d);
-  double sq = 0.0;
-  for (int i = threadIdx.x; i < d / 4; i += 256) {
-    float4 v = xr[i];
-    const float4 p = yr[i];
-    v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
-    xr[i] = v;
-    sq += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
-  }
-  sq = block_sum(sq, red);
-  const double inv = 1.0 / sqrt(sq / d + (double)eps);
-  const float4* gr = reinterpret_cast<const float4*>(gain);
-  uint2* hr = reinterpret_cast<uint2*>(h + (size_t)r * d);
-  for (int i = threadIdx.x; i < d / 4; i += 256) {
-    const float4 v = xr[i], gg = gr[i];
-    const uint32_t a = f32_to_bf16((float)((double)v.x * inv * (double)gg.x)) |
-                       ((uint32_t)f32_to_bf16((float)((double)v.y * inv * (double)gg.y)) << 16);
-    const uint32_t b = f32_to_bf16((float)((double)v.z * inv * (double)gg.z)) |
-                       ((uint32_t)f32_to_bf16((float)((double)v.w * inv * (double)gg.w)) << 16);
-    hr[i] = uint2{a, b};
-  }
-}
-
-hipError_t launch_resid_norm(float* x, const float* y, int R, int d, const float* gain,
-                             float eps, uint16_t* h, hipStream_t s) {
-  k_resid_norm<<<R, 256, 0, s>>>(x, y, R, d, gain, eps, h);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ fp32 path -----
 
 // fp32: one wave per output column n, lanes stride K; rows looped.
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
                                                   const float* __restrict__ W2, int N1, int N,
                                                   int R, int K, float* __restrict__ C, int ldc,
-                                                  int accumulate, const int32_t* __restrict__ ntok_eff,
-                                                  int M) {
+                                                  int accumulate, const float* __restrict__ rowscale,
+                                                  const int32_t* __restrict__ ntok_eff, int M) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -396,6 +554,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
     float s = 0.f;
     for (int k = lane; k < K; k += 64) s = fmaf(arow[k], wrow[k], s);
     s = wave_sum(s);
+    if (rowscale) s *= rowscale[r];
     if (lane == 0) {
       float* p = C + (size_t)r * ldc + n;
       if (ntok_eff && (r % M) >= ntok_eff[r / M]) s = 0.f;
@@ -406,11 +565,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 }
 
 hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
-                           int N, int K, float* C, int accumulate, const int32_t* ntok_eff,
-                           int M, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                           int N, int K, float* C, int accumulate, const float* rowscale,
+                           const int32_t* ntok_eff, int M, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
   if (!W2) { W2 = W; N1 = N; }
   hipExtLaunchKernelGGL(k_gemm_f32, dim3(cdiv(N, 4)), dim3(256), 0, s, e0, e1, 0, A, W, W2,
-                        N1, N, R, K, C, N, accumulate, ntok_eff, M);
+                        N1, N, R, K, C, N, accumulate, rowscale, ntok_eff, M);
   return hipGetLastError();
 }
 
@@ -447,14 +607,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   const int gmax = std::max(1, device_cus() * SPEC_GEMM_WPC / rowblocks);
   const int per = cdiv(g.ntiles, gmax);
   const int G = cdiv(g.ntiles, per);
+  if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
+  if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
+  const int mt = std::min(tiles, 4);
+  const unsigned lds = (unsigned)epi_lds_bytes(mt, g.mode, std::min(16, g.R), g.ss_np, g.hd / 2,
+                                               g.R, g.ss_in != nullptr);
   if (tiles <= 1) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<1>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<1>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
   } else if (tiles <= 2) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
   } else if (tiles <= 3) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<3>, dim3(G), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<3>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
   } else {
-    hipExtLaunchKernelGGL(k_gemm_bf16<4>, dim3(G, rowblocks), dim3(GT), 0, s, e0, e1, 0, g);
+    hipExtLaunchKernelGGL(k_gemm_bf16<4>, dim3(G, rowblocks), dim3(GT), lds, s, e0, e1, 0, g);
   }
   return hipGetLastError();
 }

@@ -65,7 +65,7 @@ struct GemmArgs {
   // QKV_ROPE
   const int32_t* pos0;
   int d, hd;
-  const double* rope_cs;  // [max_len][hd/2][2] (cos, sin) of the rotation angles by position
+  const double* rope_rows;  // [R][hd/2][2] (cos, sin) of each row's rotation angles
   uint16_t* q_out;
   uint16_t* kc;
   uint16_t* vc;
@@ -74,19 +74,32 @@ struct GemmArgs {
   // SWIGLU / GELU
   uint16_t* act_out;
   const uint16_t* zeros;  // >= 16 zero bytes (device)
+  // RMS-normalised input (QKV_ROPE, SWIGLU, GELU, STORE): A = bf16(x * g) of the rows and
+  // ss_in [R][ss_np] the partial sums of x^2 over 16-column groups; the product row r is
+  // scaled by 1 / sqrt(sum_p ss_in[r][p] / K + eps).  NULL: no scaling.
+  const float* ss_in;
+  int ss_np;
+  float eps;
+  // RESID: x [R, N] += Y; h_out [R, N] = bf16(x * gain) (the next normalised product's
+  // input) and ss_out [R][N/16] its partial sums of squares per 16-column tile
+  float* x;
+  const float* gain;
+  uint16_t* h_out;
+  float* ss_out;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };
 hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
                             uint16_t* dst, hipStream_t s);
-hipError_t launch_resid_norm(float* x, const float* y, int R, int d,
-                             const float* gain, float eps, uint16_t* h, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
-                           int N, int K, float* C, int accumulate, const int32_t* ntok_eff,
-                           int M, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                           int N, int K, float* C, int accumulate, const float* rowscale,
+                           const int32_t* ntok_eff, int M, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1);
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float eps, float* x, void* h, hipStream_t s);
+                             const float* g, float* x, void* h, float* ss, const double* rope,
+                             const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
+                             hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                                  size_t row_stride, size_t head_stride, int B, int M, int H,
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,
@@ -120,8 +133,8 @@ hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M
                        hipStream_t s);
 hipError_t launch_embed(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
                         float* x, hipStream_t s);
-hipError_t launch_rmsnorm(const float* x, const float* g, int R, int d, float eps,
-                          int dtype, void* h, hipStream_t s);
+hipError_t launch_norm_input(const float* x, const float* g, int R, int d, float eps,
+                             float* h, float* rowscale, hipStream_t s);
 hipError_t launch_rope_append(int dtype, const float* qkv, int B, int M, int H, int hd,
                               float theta, const int32_t* pos0, const int32_t* ntok_eff,
                               void* q_out, void* kcache, void* vcache, size_t row_stride,

@@ -1,6 +1,6 @@
 // Per-layer pieces of the verify pass other than the weight GEMMs: row bookkeeping,
-// embedding gather, RMSNorm (+ cast to the activation type), RoPE + KV append, the
-// FFN activation, and attention of the new rows over the KV cache.
+// embedding gather, the normalised-product input (x * g and the RMS row factor), RoPE
+// + KV append, the FFN activation, and attention of the new rows over the KV cache.
 //
 // The verify pass scores the context plus the K drafts, K+1 positions in one call
 // ([ZSM] "The algorithm"; [LENS] §2.1 step 2); keys and values of the new positions
@@ -67,58 +67,70 @@ __global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok
   for (int i = threadIdx.x; i < d; i += blockDim.x) x[(size_t)r * d + i] = Act<T>::load(e + i);
 }
 
-// bf16 models: x[r, :] = E[tok[r], :] (fp32) and h = bf16(RMSNorm(x) * g) of the first
-// layer in one pass.  One block (256 threads) per row; a thread takes 8 consecutive
-// elements at a time (one 16-byte load; d is a multiple of 128).
-__global__ __launch_bounds__(256) void k_embed_norm(const u16* __restrict__ E,
-                                                    const int32_t* __restrict__ tok, int d,
-                                                    const float* __restrict__ g, float eps,
-                                                    float* __restrict__ x, u16* __restrict__ h) {
-  __shared__ double red[4];
+// bf16 models: x[r, :] = E[tok[r], :] (fp32), the first layer's normalised-product input
+// h = bf16(x * g) and the partial sums of x^2 over each 16-column group (summed in
+// fp64, stored as fp32: ss[r][c], in column order), from which the QKV product takes its row factor
+// 1 / sqrt(mean(x^2) + eps); also the row's RoPE factors for all layers.  One block (256
+// threads) per row; a thread takes one 16-column group at a time (two 16-byte loads; d is
+// a multiple of 128).
+__global__ __launch_bounds__(256) void k_embed_norm(
+    const u16* __restrict__ E, const int32_t* __restrict__ tok, int d, const float* __restrict__ g,
+    float* __restrict__ x, u16* __restrict__ h, float* __restrict__ ss,
+    const double* __restrict__ rope, const int32_t* __restrict__ pos0, int M, int hd, int max_len,
+    double* __restrict__ rope_rows) {
   const int r = blockIdx.x;
+  {
+    // the row's RoPE factors for every layer of this forward: (cos, sin) at the row's
+    // absolute position, copied from the cache's table (rows past a sequence's tokens may
+    // sit past max_len; their q and k are never used)
+    const int half = hd >> 1;
+    const int pos = min(pos0[r / M] + r % M, max_len - 1);
+    const double2* src = reinterpret_cast<const double2*>(rope) + (size_t)pos * half;
+    double2* dst = reinterpret_cast<double2*>(rope_rows) + (size_t)r * half;
+    for (int i = threadIdx.x; i < half; i += 256) dst[i] = src[i];
+  }
   const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)tok[r] * d);
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
-  double s = 0.0;
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    const uint4 u = e[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = __uint_as_float(w[k] << 16);
-      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
-    xr[2 * c] = float4{v[0], v[1], v[2], v[3]};
-    xr[2 * c + 1] = float4{v[4], v[5], v[6], v[7]};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s += (double)v[k] * v[k];
-  }
-  s = block_sum(s, red);
-  const double inv = 1.0 / sqrt(s / d + (double)eps);
   const float4* gr = reinterpret_cast<const float4*>(g);
   uint4* hr = reinterpret_cast<uint4*>(h + (size_t)r * d);
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    const uint4 u = e[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    const float4 g0 = gr[2 * c], g1 = gr[2 * c + 1];
-    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    uint32_t o[4];
+  const int np = d / 16;
+  for (int c = threadIdx.x; c < np; c += 256) {
+    double sq = 0.0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float lo = __uint_as_float(w[k] << 16), hi = __uint_as_float(w[k] & 0xffff0000u);
-      o[k] = f32_to_bf16((float)((double)lo * inv * (double)gg[2 * k])) |
-             ((uint32_t)f32_to_bf16((float)((double)hi * inv * (double)gg[2 * k + 1])) << 16);
+    for (int half = 0; half < 2; ++half) {
+      const int c8 = 2 * c + half;  // 8-element chunk
+      const uint4 u = e[c8];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+      xr[2 * c8] = float4{v[0], v[1], v[2], v[3]};
+      xr[2 * c8 + 1] = float4{v[4], v[5], v[6], v[7]};
+      const float4 g0 = gr[2 * c8], g1 = gr[2 * c8 + 1];
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = f32_to_bf16(v[2 * k] * gg[2 * k]) |
+               ((uint32_t)f32_to_bf16(v[2 * k + 1] * gg[2 * k + 1]) << 16);
+      hr[c8] = uint4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sq += (double)v[k] * v[k];
     }
-    hr[c] = uint4{o[0], o[1], o[2], o[3]};
+    ss[(size_t)r * np + c] = (float)sq;
   }
 }
 
-// h = act(x / sqrt(mean(x^2) + eps) * g).  One block (256 threads) per row; the
-// sum of squares and the scaling are done in fp64.
-template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x,
-                                                 const float* __restrict__ g, int d, float eps,
-                                                 T* __restrict__ h) {
+// fp32 models: h = x * g and rowscale[r] = 1 / sqrt(mean(x^2) + eps), the normalised
+// product's input and row factor.  One block (256 threads) per row; the sum of squares
+// in fp64.
+__global__ __launch_bounds__(256) void k_norm_input(const float* __restrict__ x,
+                                                    const float* __restrict__ g, int d, float eps,
+                                                    float* __restrict__ h,
+                                                    float* __restrict__ rowscale) {
   __shared__ double red[4];
   const int r = blockIdx.x;
   const float* xr = x + (size_t)r * d;
@@ -126,11 +138,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x,
   for (int i = threadIdx.x; i < d; i += 256) {
     const double v = xr[i];
     s += v * v;
+    h[(size_t)r * d + i] = xr[i] * g[i];
   }
   s = block_sum(s, red);
-  const double inv = 1.0 / sqrt(s / d + (double)eps);
-  for (int i = threadIdx.x; i < d; i += 256)
-    h[(size_t)r * d + i] = Act<T>::cvt((float)((double)xr[i] * inv * (double)g[i]));
+  if (threadIdx.x == 0) rowscale[r] = (float)(1.0 / sqrt(s / d + (double)eps));
 }
 
 // RoPE on q and k of the new rows (half-split pairs (i, i + hd/2), angle =
@@ -257,12 +268,9 @@ hipError_t launch_embed(const void* embed, int dtype, const int32_t* tok_eff, in
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float* x, const float* g, int R, int d, float eps, int dtype,
-                          void* h, hipStream_t s) {
-  if (dtype == SPEC_DT_BF16)
-    k_rmsnorm<u16><<<R, 256, 0, s>>>(x, g, d, eps, (u16*)h);
-  else
-    k_rmsnorm<float><<<R, 256, 0, s>>>(x, g, d, eps, (float*)h);
+hipError_t launch_norm_input(const float* x, const float* g, int R, int d, float eps,
+                             float* h, float* rowscale, hipStream_t s) {
+  k_norm_input<<<R, 256, 0, s>>>(x, g, d, eps, h, rowscale);
   return hipGetLastError();
 }
 
@@ -297,8 +305,11 @@ hipError_t launch_attention_f32(const float* q, const float* kcache, const float
 
 
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float eps, float* x, void* h, hipStream_t s) {
-  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, eps, x, (u16*)h);
+                             const float* g, float* x, void* h, float* ss, const double* rope,
+                             const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
+                             hipStream_t s) {
+  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, x, (u16*)h, ss, rope, pos0, M,
+                                 hd, max_len, rope_rows);
   return hipGetLastError();
 }
 

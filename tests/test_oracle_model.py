@@ -141,6 +141,27 @@ def test_rmsnorm_closed_form():
     np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
 
 
+def test_normed_matmul_is_rmsnorm_then_product():
+    """N(x, g) W^T: without bf16 rounding it is RMSNorm(x) * g times W^T (the row factor
+    commutes with the product); with bf16 rounding of the input it stays within the
+    rounding bound of the same product formed from bf16(RMSNorm(x) * g)."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((5, 96)) * rng.uniform(0.1, 30.0, (5, 1))
+    g = rng.uniform(0.5, 1.5, 96)
+    w = rng.standard_normal((40, 96)) * 0.02
+    ident = lambda t: np.asarray(t, dtype=np.float64)
+    got = model.normed_matmul(x, g, w, 1e-5, ident)
+    ref = model.rmsnorm(x, g, 1e-5) @ w.T
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+    # bf16 inputs: both orders round each element once (relative error <= 2^-9), so
+    # they differ by at most 2 * 2^-9 * sum_k |RMSNorm(x)_k g_k w_nk| per output
+    gotb = model.normed_matmul(x, g, w, 1e-5, model.round_bf16)
+    other = model.round_bf16(model.rmsnorm(x, g, 1e-5)) @ w.T
+    bound = 2 * 2.0 ** -9 * (np.abs(model.rmsnorm(x, g, 1e-5)) @ np.abs(w).T) + 1e-15
+    assert np.all(np.abs(gotb - other) <= bound)
+    assert np.any(gotb != other)   # the rounding point did move
+
+
 def test_rope_properties():
     rng = np.random.default_rng(8)
     hd = 32
