@@ -116,8 +116,8 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   const size_t e = elt_bytes(c);
   const size_t d = c.d_model, F = c.d_ffn, V = c.vocab;
   const size_t ffn_out = c.ffn_kind == SPEC_FFN_SWIGLU ? 2 * F : F;
-  // attention splits: at most one per 4 blocks of 32 positions (any call shape)
-  const size_t nsplit = (size_t)cdiv(cdiv(max_len, 32), 4);
+  // attention splits: the bound of the split count for this call shape
+  const size_t nsplit = (size_t)attn_max_splits(B, c.n_heads, M, max_len);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;

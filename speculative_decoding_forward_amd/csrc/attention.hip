@@ -15,8 +15,10 @@
 // Every wave load is therefore 1 KB contiguous.
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
-// (b, h) and one group of up to 16 queries; its 4 waves take the blocks round-robin,
-// keep two blocks of K and V in flight, and run an online softmax per query.  The
+// (b, h) and one group of up to 16 queries; the split count makes the grid one
+// workgroup per compute unit.  Its waves (8 for head_dim 128) take the blocks
+// round-robin, keep two blocks of K and V in flight each -- with a split's blocks thus
+// all requested at once -- and run an online softmax per query.  The
 // wave states merge in LDS; with more than one split the workgroup partial goes to
 // global memory and the last workgroup of (b, h, qg) to finish merges them in split
 // order and writes the bf16 output.  P enters the second product as bf16 hi + lo
@@ -31,7 +33,17 @@
 
 namespace specdec {
 
-constexpr int AW = 4;    // waves per workgroup
+// Waves per workgroup and blocks each wave keeps in flight (ring depth).  With one
+// workgroup per compute unit the ring can be deep: a split's blocks are then all
+// requested at once.
+#ifndef SPEC_ATTN_WAVES
+#define SPEC_ATTN_WAVES 8
+#endif
+#ifndef SPEC_ATTN_RING
+#define SPEC_ATTN_RING 2
+#endif
+template <int HD> constexpr int attn_waves() { return HD == 128 ? SPEC_ATTN_WAVES : 4; }
+template <int HD> constexpr int attn_ring() { return HD == 128 ? SPEC_ATTN_RING : 2; }
 constexpr int AQ = 16;   // queries per group
 constexpr int AKB = 32;  // keys per block
 
@@ -39,12 +51,12 @@ __device__ __forceinline__ bf16x8 ldfrag(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-template <int HD>
+template <int HD, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
 __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     const u16* __restrict__ q, int M, int H, const u16* __restrict__ kc,
     const u16* __restrict__ vc, size_t row_stride, size_t head_stride,
     const int32_t* __restrict__ pos0, const int32_t* __restrict__ ntok_eff,
-    float* __restrict__ part, unsigned* __restrict__ counters, int nsplit, int npw,
+    float* __restrict__ part, unsigned* __restrict__ counters, int nsplit, int bps,
     u16* __restrict__ out) {
   constexpr int NS = HD / 32;  // K slices (MFMAs per 16-key tile)
   constexpr int NT = HD / 16;  // dim tiles of O
@@ -59,7 +71,8 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   const int nq = ntok_eff[b];
   const int p0 = pos0[b];
   const int len_end = p0 + nq;
-  const int bps = AW * npw;  // blocks per split
+  // blocks of this wave in its split: wv, wv + AW, ... below bps
+  const int nmine = wv < bps ? (bps - 1 - wv) / AW + 1 : 0;
   const int nblk = cdiv(len_end, AKB);
   const int n_active = cdiv(nblk, bps);
   const int d = H * HD;
@@ -86,15 +99,13 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   for (int s = 0; s < NS; ++s) qf[s] = ldfrag(qrow + 32 * s);
   const int qpos = p0 + jq;  // the query's cache position
 
-  // Ring of two blocks.  Block i of this wave is split*bps + wv + AW*i; a load past the
-  // wave's share or the row's end re-reads the wave's last block in bounds (a cache
-  // hit) and the scores of a block outside the share are masked, so no load sits
-  // behind a branch.
-  bf16x8 kf[2][2][NS];
-  bf16x8 vf[2][NT];
+  // Ring of RING blocks.  Block i of this wave is split*bps + wv + AW*i (i < nmine); a
+  // block past the row's end is clamped to its last block (in bounds) and masked.
+  bf16x8 kf[RING][2][NS];
+  bf16x8 vf[RING][NT];
   const int blk0 = split * bps + wv;
   auto load = [&](int slot, int i) {
-    const int blk = min(blk0 + AW * min(i, npw - 1), nblk - 1);
+    const int blk = min(blk0 + AW * min(i, max(nmine - 1, 0)), nblk - 1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
 #pragma unroll
   for (int u = 0; u < NT; ++u) o[u] = floatx4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int slot, int i) {
-    const bool in_share = i < npw;
+    const bool in_share = i < nmine;
     const int kb = (blk0 + AW * i) * AKB;  // first key position of the block
     float sc[2][4];
 #pragma unroll
@@ -171,24 +182,27 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
       o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf[slot][u], o[u], 0, 0, 0);
     }
   };
-  load(0, 0);
-  __builtin_amdgcn_sched_barrier(0);  // slot 0 issued first, as in the steady state
-  load(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  // scheduling fences: a slot is refilled right after its use, and the next slot's use
-  // stays behind that refill (so two blocks are always in flight)
-  for (int i = 0; i < npw; i += 2) {
-    compute(0, i);
-    __builtin_amdgcn_sched_barrier(0);
-    load(0, i + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, i + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(1, i + 3);
+  // Loads are only issued for the wave's own blocks (a uniform branch per wave); the
+  // scheduling fences keep a slot's refill right behind its use, so RING blocks stay
+  // in flight.
+#pragma unroll
+  for (int r = 0; r < RING; ++r) {
+    if (r < nmine) load(r, r);
     __builtin_amdgcn_sched_barrier(0);
   }
+  for (int i0 = 0; i0 < nmine; i0 += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      if (i0 + r < nmine) {
+        compute(r, i0 + r);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0 + r + RING < nmine) load(r, i0 + r + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
 
-  // wave states -> LDS; merge the 4 waves: thread -> (query jj, dims)
+  // wave states -> LDS; merge the waves: thread -> (query jj, dims)
   if (lane < AQ) {
     wm[wv][lane] = m;
     wl[wv][lane] = l;
@@ -198,8 +212,9 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
 #pragma unroll
     for (int e = 0; e < 4; ++e) wo[wv][4 * g + e][16 * u + nl] = o[u][e];
   __syncthreads();
-  constexpr int TPQ = AW * 64 / AQ;  // threads per query (16)
-  constexpr int DPT = HD / TPQ;      // dims per thread (8 or 4)
+  constexpr int TPQ = AW * 64 / AQ;  // threads per query (16 or 32)
+  constexpr int DPT = HD / TPQ;      // dims per thread (4)
+  static_assert(DPT == 4 || DPT == 8, "merge layout");
   const int jj = threadIdx.x / TPQ, tt = threadIdx.x % TPQ;
   const int j = qg * AQ + jj;
   float mx = -INFINITY;
@@ -303,19 +318,29 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   if (threadIdx.x == 0) counters[cidx] = 0u;
 }
 
-// Blocks per wave: the smallest power of two that fits the grid over the cache capacity
-// in one round of resident workgroups (two per compute unit), so no workgroup waits for
-// a second round; a wave streams its blocks through its two-block ring.
-int attn_npw(int B, int H, int M, int max_len) {
-  const long blocks = cdiv(max_len, AKB), groups = (long)B * H * cdiv(M, AQ);
-  const long resident = 2L * device_cus();
-  int npw = 1;
-  while (npw < 1024 && groups * ((blocks + AW * npw - 1) / (AW * npw)) > resident) npw <<= 1;
-  return npw;
+// Upper bound of attn_nsplit for any device (workspace sizing): one split per block and
+// at most kAttnMaxCUs workgroups.
+int attn_max_splits(int B, int H, int M, int max_len) {
+  const int groups = B * H * cdiv(M, AQ);
+  return std::max(1, std::min(cdiv(max_len, AKB), cdiv(kAttnMaxCUs, groups)));
 }
 
+// Splits per (row, head, query group): as many as make the grid one workgroup per
+// compute unit (a CU holding two workgroups streams its two shares at half the rate
+// and finishes last), and at most one per block.  A split takes `bps` consecutive
+// blocks (attn_bps), the workgroup's waves round-robin.
 int attn_nsplit(int B, int H, int M, int max_len) {
-  return cdiv(cdiv(max_len, AKB), AW * attn_npw(B, H, M, max_len));
+  const int blocks = cdiv(max_len, AKB), groups = B * H * cdiv(M, AQ);
+  int ns = std::max(1, std::min(device_cus(), kAttnMaxCUs) / groups);
+  ns = std::min(ns, attn_max_splits(B, H, M, max_len));
+  // the same split count with fewer blocks per split would leave splits empty: shrink
+  // it to the number that the per-split block count really needs
+  const int bps = cdiv(blocks, ns);
+  return cdiv(blocks, bps);
+}
+
+int attn_bps(int B, int H, int M, int max_len) {
+  return cdiv(cdiv(max_len, AKB), attn_nsplit(B, H, M, max_len));
 }
 
 int attn_groups(int M) { return cdiv(M, AQ); }
@@ -325,17 +350,17 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
                                  const int32_t* pos0, const int32_t* ntok_eff, float* part,
                                  unsigned* counters, int max_len, u16* out, hipStream_t s,
                                  hipEvent_t e0, hipEvent_t e1) {
-  const int npw = attn_npw(B, H, M, max_len);
+  const int bps = attn_bps(B, H, M, max_len);
   const int nsplit = attn_nsplit(B, H, M, max_len);
   const dim3 grid(nsplit, H, B * attn_groups(M));
   if (hd == 128)
-    hipExtLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(AW * 64), 0, s, e0, e1, 0, q, M, H, kc,
+    hipExtLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(attn_waves<128>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
                           vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          npw, out);
+                          bps, out);
   else if (hd == 64)
-    hipExtLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(AW * 64), 0, s, e0, e1, 0, q, M, H, kc,
+    hipExtLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(attn_waves<64>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
                           vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          npw, out);
+                          bps, out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -105,7 +105,9 @@ hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const ui
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,
                                  float* part, unsigned* counters, int max_len, uint16_t* out,
                                  hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+constexpr int kAttnMaxCUs = 1024;                     // bound on the CUs a split grid uses
 int attn_nsplit(int B, int H, int M, int max_len);  // splits per (row, head, group)
+int attn_max_splits(int B, int H, int M, int max_len);  // bound of attn_nsplit (workspace)
 int attn_groups(int M);                               // query groups per row
 int device_cus();                                     // compute units of the device
 hipError_t launch_kv_convert(uint16_t* cache, uint16_t* nat, int L, int B, int H, int hd, int n,
