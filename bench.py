@@ -14,8 +14,10 @@ roofline object covers the dominant kernel (the weight-streaming GEMM), timed li
 HIP events on its launch stream over the timed rounds.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +27,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of
+# `bench.py --verify-only` scaled by the same counters on a copy of known size; used
+# only while the kernel sources still hash to the value recorded with the figures.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_verify_7b_b1_k5_traffic.md")
+GEMM_SOURCES = ["speculative_decoding_forward_amd/csrc/gemm.hip",
+                "speculative_decoding_forward_amd/csrc/common.h",
+                "speculative_decoding_forward_amd/csrc/internal.h"]
 
 
 def parse():
@@ -38,7 +47,36 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--verify-only", action="store_true",
+                    help="target model only: prefill, then --steps eager verify passes "
+                         "(each rolled back); for counter runs of the verify GEMMs")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="copy MIB MiB device-to-device three times and exit (known bytes "
+                         "for scaling the HBM counters)")
     return ap.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Bytes per GEMM launch from the committed counter summary, or None when it is absent
+    or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_sources_sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    if not src or not val or src.group(1) != gemm_source_hash():
+        return None
+    return float(val.group(1))
 
 
 def gemm_bytes_per_verify(shape, R):
@@ -151,6 +189,43 @@ def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
     }
 
 
+def verify_only(args, wl):
+    """Target model only: prefill the context, then --steps eager verify passes over K+1
+    new tokens per row, each rolled back so every pass sees the same cache length."""
+    import torch
+
+    from speculative_decoding_forward_amd import binding, synth
+
+    B = args.batch or wl.batch
+    K = args.K or wl.K
+    dev = "cuda"
+    W = synth.make_weights(wl.target, seed=args.seed, model_id=synth.TARGET, device=dev)
+    m = binding.Model(wl.target, W)
+    del W
+    max_len = wl.ctx + 2 * (K + 1) + 2
+    kv = binding.KVCache(wl.target, B, max_len, dev)
+    ws = m.workspace(B, 64, max_len, device=dev)
+    ctx = synth.context_ids(args.seed, B, wl.ctx, wl.target.vocab)
+    lg = torch.empty((B, 64, wl.target.vocab), device=dev)
+    for s0 in range(0, wl.ctx, 64):
+        tok = torch.from_numpy(np.ascontiguousarray(ctx[:, s0:s0 + 64]).astype(np.int32)).to(dev)
+        binding.verify_forward(m, kv, tok, lg[:, :tok.shape[1]].contiguous(), ws)
+    torch.cuda.synchronize()
+    base = kv.len.clone()
+    new = torch.from_numpy(synth.context_ids(args.seed + 1, B, K + 1, wl.target.vocab)
+                           .astype(np.int32)).to(dev)
+    logits = torch.empty((B, K + 1, wl.target.vocab), device=dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        binding.verify_forward(m, kv, new, logits, ws)
+        kv.rollback(base)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"mode": "verify-only", "workload": args.workload, "batch": B, "K": K,
+                      "passes": args.steps, "ms_per_pass": dt / args.steps * 1e3,
+                      "kernel_sources_sha256": gemm_source_hash()}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,7 +238,19 @@ def main():
     from speculative_decoding_forward_amd import binding, rounds, synth
 
     assert torch.cuda.is_available(), "no GPU"
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
     wl = synth.WORKLOADS[args.workload]
+    if args.verify_only:
+        verify_only(args, wl)
+        return
     B = args.batch or wl.batch
     K = args.K or wl.K
     knobs = (wl.temperature, wl.top_k, wl.top_p)
@@ -216,26 +303,24 @@ def main():
     torch.cuda.synchronize()
     verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
-    # dominant kernel: the weight-streaming GEMM, timed by HIP events attached to its
-    # own dispatch packets (hipExtLaunchKernelGGL) over eager rounds that continue the
-    # same sequence
+    # dominant kernel: the verify pass's weight-streaming GEMM, timed by HIP events
+    # attached to its own dispatch packets (hipExtLaunchKernelGGL) over eager verify
+    # passes, each rolled back to the same cache length
     n_meas = max(4, args.steps // 2)
-    next_round = int(dec.round_dev.item())
+    torch.cuda.synchronize()
     binding.timing_enable(True)
     binding.timing_read()
     for i in range(n_meas):
-        dec.step(next_round + i)
+        dec.verify_phase()
+        dec.tkv.rollback(saved_len)
     torch.cuda.synchronize()
     binding.timing_enable(False)
     gemm_ms, gemm_n, attn_ms, attn_n = binding.timing_read()
 
     R_v = B * (K + 1)
     gb_v, gn_v = gemm_bytes_per_verify(wl.target, R_v)
-    gb_d0, gn_d0 = gemm_bytes_per_verify(wl.draft, B * 2)
-    gb_d1, gn_d1 = gemm_bytes_per_verify(wl.draft, B)
-    gemm_bytes = n_meas * (gb_v + gb_d0 + (K - 1) * gb_d1)
-    assert gemm_n == n_meas * (gn_v + gn_d0 + (K - 1) * gn_d1), (gemm_n,)
-    gemm_avg_bytes = gemm_bytes / gemm_n
+    assert gemm_n == n_meas * gn_v, (gemm_n,)
+    gemm_avg_bytes = gb_v / gn_v
     gemm_avg_s = gemm_ms / 1e3 / gemm_n
     achieved = gemm_avg_bytes / gemm_avg_s / 1e9
     vb = verify_bytes(wl.target, B, K, (len_start + len_end) / 2)
@@ -269,12 +354,16 @@ def main():
         "verify_bytes": vb,
         "tokens_per_round_per_row": tokens / (B * args.steps),
         "alpha_measured": alpha_hat,
-        "attention_ms_per_round": attn_ms / n_meas,
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_bf16 (weight-streaming GEMM)",
+        "verify_attention_ms": attn_ms / n_meas,
+        "verify_gemm_ms": gemm_ms / n_meas,
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_gemm_bf16 (verify-pass weight-streaming GEMM, 4 per layer "
+                               "+ LM head)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
                      "bytes_per_launch": gemm_avg_bytes,
-                     "avg_launch_us": gemm_avg_s * 1e6, "launches": gemm_n},
+                     "avg_launch_us": gemm_avg_s * 1e6, "launches": gemm_n,
+                     "kernel_sources_sha256": gemm_source_hash()},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, B, K, tokens / args.steps, args.cpu_seconds)
