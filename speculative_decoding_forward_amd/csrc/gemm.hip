@@ -10,13 +10,14 @@
 // flight; the matrix cores are used because the work is a dense contraction (R rows
 // padded to 16-row MFMA tiles), not because they bound the time.
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16.  A workgroup of 8 waves owns 16 output columns
-// (16 rows of W) and up to 64 rows of A; the waves split K in 128-wide super-steps,
-// round-robin, and the 8 fp32 partials are summed in LDS in a fixed order.  In a
-// super-step, MFMA s (s = 0..3) covers k in [128i + 32s, 128i + 32s + 32) and lane l
-// holds W row (l % 16), elements 8(l / 16) .. +8 of that range, so one load
-// instruction reads 64 contiguous bytes of each of 16 rows.  Each wave keeps PF
-// super-steps of W loads in flight (a register ring, statically indexed).
+// bf16 path: v_mfma_f32_16x16x32_bf16.  A workgroup has 4 streaming waves and one
+// epilogue wave; it owns column tiles of 16 output columns (16 rows of W) and up to 64
+// rows of A.  The streaming waves split K in 128-wide super-steps, round-robin, and
+// their fp32 partials are summed in LDS in a fixed order.  In a super-step, MFMA s
+// (s = 0..3) covers k in [128i + 32s, 128i + 32s + 32) and lane l holds W row (l % 16),
+// elements 8(l / 16) .. +8 of that range; with the packed layout below one load
+// instruction reads 1 KB contiguous.  Each wave requests the super-step ahead before
+// multiplying the current one (a register ring, statically indexed).
 //
 // Epilogues (selected per launch):
 //   STORE      Y -> fp32 C (rows past a sequence's token count stored as 0): LM head
@@ -49,7 +50,7 @@ namespace specdec {
 #define SPEC_GEMM_WAVES 4  // streaming waves per workgroup (plus one epilogue wave)
 #endif
 #ifndef SPEC_GEMM_RING
-#define SPEC_GEMM_RING 2
+#define SPEC_GEMM_RING 1  // steps requested ahead of the one being multiplied
 #endif
 #ifndef SPEC_GEMM_WPC
 #define SPEC_GEMM_WPC 2  // resident workgroups per compute unit the grid is sized for
@@ -383,7 +384,7 @@ __device__ __forceinline__ void epi_barrier() {
 // resident at once; the larger row tiles accept one workgroup per CU.
 template <int MT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
-  constexpr int P = MT <= 2 ? SPEC_GEMM_RING : (SPEC_GEMM_RING > 2 ? 2 : SPEC_GEMM_RING);
+  constexpr int P = SPEC_GEMM_RING;
   __shared__ floatx4 part[2][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
   __shared__ double rowscale[MT * 16];
@@ -475,8 +476,9 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wf[P][4];
-  bf16x8 af[P][MT][4];
+  constexpr int Q = P + 1;  // register buffers: P steps in flight while one is multiplied
+  bf16x8 wf[Q][4];
+  bf16x8 af[Q][MT][4];
   const u16* zblk = g.zeros;
   // issue stream: tile iteration it, step is; a step past the wave's last one in a tile,
   // or past the workgroup's last tile, re-reads an in-bounds W segment (cache hit) and
@@ -520,18 +522,20 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
       for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  // Rounds of P steps; the last round's refills read in-bounds W past the end (cache
-  // hits, never consumed) so that the loop body is the only copy of the tile code.
+  // Rounds of Q steps.  Each step first requests the step P ahead (into the buffer
+  // multiplied last) and then multiplies its own buffer, so the requests never wait
+  // behind the MFMA chain.  The last round's requests read in-bounds W past the end
+  // (cache hits, never multiplied), so the loop body is the only copy of the tile code.
   const int F = nt * S;  // steps of this wave
-  const int T = (F + P - 1) / P;
+  const int T = (F + Q - 1) / Q;
 #pragma unroll
   for (int u = 0; u < P; ++u) issue(u);
   for (int t = 0; t < T; ++t) {
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
+    for (int u = 0; u < Q; ++u) {
+      issue((u + P) % Q);
+      __builtin_amdgcn_sched_barrier(0);
       consume(u);
-      issue(u);
-      // keep each refill right behind the use of its slot (no drain per round)
       __builtin_amdgcn_sched_barrier(0);
     }
   }
