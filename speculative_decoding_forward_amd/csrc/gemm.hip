@@ -53,7 +53,7 @@ namespace specdec {
 #define SPEC_GEMM_RING 1  // steps requested ahead of the one being multiplied
 #endif
 #ifndef SPEC_GEMM_WPC
-#define SPEC_GEMM_WPC 2  // resident workgroups per compute unit the grid is sized for
+#define SPEC_GEMM_WPC 1  // workgroups per compute unit the grid is sized for
 #endif
 constexpr int GW = SPEC_GEMM_WAVES;  // streaming waves per workgroup
 constexpr int GT = (GW + 1) * 64;    // threads per workgroup
@@ -379,9 +379,10 @@ __device__ __forceinline__ void epi_barrier() {
 // (double-buffered by tile parity) and meets the others at one barrier; the epilogue
 // wave then sums the partials and runs the epilogue while the streaming waves go on with
 // the next tile.
-// Register budget: two workgroups of GW + 1 waves per CU put two waves of each on one
-// SIMD, so the kernel must fit four waves per SIMD (<= 128 VGPRs) for the grid to be
-// resident at once; the larger row tiles accept one workgroup per CU.
+// Residency: the grid is sized for one workgroup per compute unit (a CU holding two
+// streams both shares through one memory pipeline and finishes last).  Were it sized
+// for two, two workgroups of GW + 1 waves put two waves of each on one SIMD, and the
+// kernel would have to fit four waves per SIMD (<= 128 VGPRs) to be resident at once.
 template <int MT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   constexpr int P = SPEC_GEMM_RING;
@@ -601,8 +602,9 @@ int device_cus() {
   return cached[dev];
 }
 
-// Grid: G persistent workgroups per row block, G chosen so that the tiles divide as
-// evenly as possible (every workgroup gets ceil(tiles / G) or one fewer).
+// Grid: G persistent workgroups per row block, at most one per compute unit, G chosen
+// so that the tiles divide as evenly as possible (every workgroup gets ceil(tiles / G)
+// or one fewer).
 hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   GemmArgs g = g0;
   g.ntiles = gemm_blocks_x(g);
