@@ -371,7 +371,8 @@ __device__ __forceinline__ void epi_barrier() {
 }
 
 // Persistent weight-streaming GEMM.  Workgroup (bx, by) owns row block by (MT*16 rows
-// of A) and the column tiles bx, bx + G, bx + 2G, ... (G = gridDim.x).  It has GW
+// of A) and the column-tile groups bx, bx + G, bx + 2G, ... (G = gridDim.x; a group is
+// NT consecutive 16-column tiles, see below).  It has GW
 // streaming waves and one epilogue wave.  The streaming waves split K: wave wv takes
 // 128-wide super-steps wv, wv + GW, ... of every tile, so its steps form one flat
 // stream over (tile, step) and its register ring of P steps runs across tile
@@ -383,17 +384,23 @@ __device__ __forceinline__ void epi_barrier() {
 // streams both shares through one memory pipeline and finishes last).  Were it sized
 // for two, two workgroups of GW + 1 waves put two waves of each on one SIMD, and the
 // kernel would have to fit four waves per SIMD (<= 128 VGPRs) to be resident at once.
-template <int MT>
+// NT: column tiles multiplied per step.  With 32 or more rows every A fragment is used
+// for NT tiles at once, which divides the A reads per weight byte (with three or four
+// row tiles the A reads through L1, not HBM, bound the kernel).  Every output element
+// still accumulates its K steps in the same order as with NT = 1.
+template <int MT, int NT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   constexpr int P = SPEC_GEMM_RING;
-  __shared__ floatx4 part[2][GW][MT][64];
+  static_assert(MT > 1 || NT == 1, "one row tile uses single column tiles");
+  __shared__ floatx4 part[2][NT][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
   __shared__ double rowscale[MT * 16];
   extern __shared__ float4 epi_dyn[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bx = blockIdx.x, G = gridDim.x;
   const int r0 = blockIdx.y * (MT * 16);
-  const int nt = (g.ntiles - bx + G - 1) / G;  // tiles of this workgroup (>= 1)
+  const int ngroups = g.ntiles / NT;
+  const int nt = (ngroups - bx + G - 1) / G;  // tile groups of this workgroup (>= 1)
   if (wv == GW) {
     const int rows = min(MT * 16, g.R - r0);  // >= 1
     const int np = g.ss_np, half = g.hd >> 1;
@@ -448,7 +455,10 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     wave_lds_sync();
     for (int ct = 0; ct < nt; ++ct) {
       epi_barrier();
-      gemm_tile_epilogue<MT>(g, bx + ct * G, r0, part[ct & 1], rowinfo, rowscale, L, lane);
+#pragma unroll 1
+      for (int n = 0; n < NT; ++n)
+        gemm_tile_epilogue<MT>(g, (bx + ct * G) * NT + n, r0, part[ct & 1][n], rowinfo, rowscale,
+                               L, lane);
       if constexpr (MT == 1) {
         if (g.mode == EPI_RESID && ct + 1 < nt) {
           wave_lds_sync();
@@ -473,25 +483,30 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     aok[mt] = r < R;
     arow[mt] = g.A + (size_t)(aok[mt] ? r : 0) * g.lda + 8 * gq;
   }
-  floatx4 acc[MT];
+  floatx4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int Q = P + 1;  // register buffers: P steps in flight while one is multiplied
-  bf16x8 wf[Q][4];
+  bf16x8 wf[Q][NT][4];
   bf16x8 af[Q][MT][4];
   const u16* zblk = g.zeros;
   // issue stream: tile iteration it, step is; a step past the wave's last one in a tile,
   // or past the workgroup's last tile, re-reads an in-bounds W segment (cache hit) and
   // pairs it with zero A fragments, so every wave runs the same branch-free schedule.
   int it = 0, is = 0;
-  const u16* wp = g.W + (size_t)bx * tile_elems + 8 * lane;
+  const u16* wp = g.W + (size_t)bx * NT * tile_elems + 8 * lane;
   auto issue = [&](int slot) {
     const bool valid = is <= last_step && wact && it < nt;
     const int js = wact ? wv + (is <= last_step ? is : last_step) * GW : 0;  // super-step
     const int kb = js * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wf[slot][s] = ld8_nt(wp + js * 2048 + 512 * s, true);
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        wf[slot][n][s] = ld8_nt(wp + n * tile_elems + js * 2048 + 512 * s, true);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     if (++is == S) {
       is = 0;
       ++it;
-      if (it < nt) wp += (size_t)G * tile_elems;
+      if (it < nt) wp += (size_t)G * NT * tile_elems;
     }
   };
   int ct = 0, cs = 0;  // consume stream: tile iteration, step
@@ -508,19 +523,25 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mt][s], wf[slot][s],
-                                                          acc[mt], 0, 0, 0);
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mt][s], wf[slot][n][s],
+                                                               acc[mt][n], 0, 0, 0);
     if (++cs == S) {
       cs = 0;
       if (ct < nt) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) part[ct & 1][wv][mt][lane] = acc[mt];
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) part[ct & 1][n][wv][mt][lane] = acc[mt][n];
         __syncthreads();
       }
       ++ct;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
   // Rounds of Q steps.  Each step first requests the step P ahead (into the buffer
@@ -611,22 +632,36 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   const int tiles = cdiv(g.R, 16);
   const int rowblocks = tiles <= 3 ? 1 : cdiv(g.R, 64);
   const int gmax = std::max(1, device_cus() * SPEC_GEMM_WPC / rowblocks);
-  const int per = cdiv(g.ntiles, gmax);
-  const int G = cdiv(g.ntiles, per);
+  // Column tiles per step.  With 32+ rows a pair of tiles streamed together takes about
+  // 1.5 times as long as one tile (measured at 48 rows: the A fragments are read once
+  // for both), so pairs are used when the busiest workgroup's time in tile units,
+  // 1.5 * ceil(pairs / gmax), is below ceil(tiles / gmax).
+  int NTc = 1;
+  if (tiles >= 2 && g.ntiles % 2 == 0 && 3 * cdiv(g.ntiles / 2, gmax) < 2 * cdiv(g.ntiles, gmax))
+    NTc = 2;
+  const int ngroups = g.ntiles / NTc;
+  const int per = cdiv(ngroups, gmax);
+  const int G = cdiv(ngroups, per);
   if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
   const unsigned lds = (unsigned)epi_lds_bytes(mt, g.mode, std::min(16, g.R), g.ss_np, g.hd / 2,
                                                g.R, g.ss_in != nullptr);
+#define SPEC_GEMM_LAUNCH(MT_, NT_, GY)                                                     \
+  hipExtLaunchKernelGGL(k_gemm_bf16<MT_, NT_>, dim3(G, GY), dim3(GT), lds, s, e0, e1, 0, g)
   if (tiles <= 1) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<1>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
+    SPEC_GEMM_LAUNCH(1, 1, 1);
   } else if (tiles <= 2) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
+    if (NTc == 2) SPEC_GEMM_LAUNCH(2, 2, 1);
+    else SPEC_GEMM_LAUNCH(2, 1, 1);
   } else if (tiles <= 3) {
-    hipExtLaunchKernelGGL(k_gemm_bf16<3>, dim3(G), dim3(GT), lds, s, e0, e1, 0, g);
+    if (NTc == 2) SPEC_GEMM_LAUNCH(3, 2, 1);
+    else SPEC_GEMM_LAUNCH(3, 1, 1);
   } else {
-    hipExtLaunchKernelGGL(k_gemm_bf16<4>, dim3(G, rowblocks), dim3(GT), lds, s, e0, e1, 0, g);
+    if (NTc == 2) SPEC_GEMM_LAUNCH(4, 2, rowblocks);
+    else SPEC_GEMM_LAUNCH(4, 1, rowblocks);
   }
+#undef SPEC_GEMM_LAUNCH
   return hipGetLastError();
 }
 
