@@ -16,11 +16,14 @@
 // values, VPT = ceil(V/1024) per thread in registers, element i = t*1024 + tid
 // (coalesced loads).  Each row is read from HBM exactly once.
 //
-// Numerics: exponentials in fp32, all sums (softmax normaliser, top-p masses, the
-// residual mass and the inverse-CDF running sums) in fp64 with a fixed reduction
-// order; top-k / top-p thresholds are found by radix select on an order-preserving
-// key of the LOGIT (so ties are exactly the equal logits), with integer (count or
-// 2^52 fixed-point mass) histograms, so the selection is deterministic.
+// Numerics: exponentials in fp32, computed once per element; all sums (softmax
+// normaliser, kept mass, the residual mass and the inverse-CDF running sums) in fp64
+// or exact integers with a fixed reduction order.  Thresholds are found by radix
+// select on an order-preserving 32-bit key with integer histograms, so the selection
+// is deterministic: top-k on the key of the logit (ties are equal logits), top-p on
+// the key of the unnormalised probability e = exp((l - max) / T) with each element's
+// mass e/S as a 2^-52 fixed-point integer (ties are equal probabilities, the rule
+// "keep every token whose probability reaches the threshold's").
 #include <float.h>
 
 #include "common.h"
@@ -31,20 +34,70 @@ namespace specdec {
 constexpr int VT = 1024;   // threads per vocab workgroup
 constexpr int NWV = VT / 64;
 constexpr int MAXVPT = 32;  // V <= 32768
+constexpr int RBINS = 2048;  // radix digit bins (11-bit digits)
 
 struct VocabLDS {
   double dred[NWV];
   float fred[NWV];
   int ired[NWV];
-  unsigned long long hist[256];
+  unsigned long long hist[RBINS];
+  unsigned long long wsuf[NWV];
   double scan[NWV];
   float w[MAXVPT * VT];  // inverse-CDF weights in token-id order
-  double bcast_d[4];
+  unsigned long long bcast_ull[3];
   int bcast_i[4];
-  unsigned long long bcast_ull;
   float px, qx;
   float zero;  // always 0; read inside loops so per-element work is not hoisted
 };
+
+// Lane shuffles whose address is computed from a lane id read afresh each time (the
+// asm is volatile): the compiler would otherwise keep one address register per
+// shuffle pattern live through the whole kernel, and with a 32-value row in registers
+// those spill.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+__device__ __forceinline__ uint64_t shfl_src_u64(uint64_t v, int src) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(v >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ double shfl_src_d(double v, int src) {
+  return __longlong_as_double((long long)shfl_src_u64((uint64_t)__double_as_longlong(v), src));
+}
+__device__ __forceinline__ float shfl_xor_f(float v, int o) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_fresh() ^ o) << 2, __float_as_int(v)));
+}
+// value of lane - o (lanes below o read a wrapped lane; callers mask those)
+__device__ __forceinline__ double shfl_up_d(double v, int o) {
+  return shfl_src_d(v, (lane_fresh() - o) & 63);
+}
+// value of lane + o (wrapped; callers mask)
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int o) {
+  return shfl_src_u64(v, (lane_fresh() + o) & 63);
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += shfl_src_d(v, lane_fresh() ^ o);
+  return v;
+}
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum_d(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < NWV; ++i) t += red[i];
+  return t;
+}
 
 // order-preserving key of a float (-0 folded onto +0)
 __device__ __forceinline__ uint32_t okey(float f) {
@@ -53,78 +106,85 @@ __device__ __forceinline__ uint32_t okey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Largest key t such that the total weight of kept elements (logit > -inf) with
-// key >= t reaches `target` (4 passes of 8-bit digits, integer histograms in LDS).
-// Returns 0 (keep everything) if all kept elements together do not reach it.
-template <int VPT, typename WeightF>
-__device__ __forceinline__ uint32_t radix_select(const float (&v)[VPT], WeightF wf,
-                                                 unsigned long long target, VocabLDS& sh) {
-  const int tid = threadIdx.x;
+struct RadixResult {
+  uint32_t t;                // threshold key: keep key >= t
+  unsigned long long kept;   // total weight of the kept elements
+  bool all;                  // the target was not reached: keep everything
+};
+
+// Largest key t such that the total weight of the participating elements with key
+// >= t reaches `target` (> 0).  kw(x, key, weight) says whether element x takes part
+// and gives its key and integer weight.  Three passes over 11-, 11- and 10-bit digits
+// (high to low), each an LDS histogram of the elements whose key matches the digits
+// chosen so far, a block-wide suffix scan over the 2048 bins, and the unique bin
+// where the running weight crosses the target.
+template <int VPT, typename KW>
+__device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KW kw,
+                                                    unsigned long long target, VocabLDS& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t prefix = 0;
-  unsigned long long above = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += VT) sh.hist[i] = 0ull;
+  unsigned long long above = 0, kept = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    // digit bits [shift, hs); bits [hs, 32) were fixed by the earlier passes
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int hs = pass == 0 ? 31 : (pass == 1 ? 21 : 10);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    sh.hist[2 * tid] = 0ull;
+    sh.hist[2 * tid + 1] = 0ull;
+    if (tid == 0) sh.bcast_i[0] = -1;
     __syncthreads();
-    // keys and weights are recomputed every pass (x = v + 0 read from LDS) rather
-    // than kept live across passes, which would not fit the register budget
     const float zero = sh.zero;
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
-      const float x = v[t] + zero;
-      if (x == -INFINITY) continue;
-      const uint32_t k = okey(x);
-      const bool match = pass == 0 ? true : ((k >> (shift + 8)) == (prefix >> (shift + 8)));
-      if (match) atomicAdd(&sh.hist[(k >> shift) & 255u], wf(x));
-      __builtin_amdgcn_sched_barrier(0);
+      uint32_t k;
+      unsigned long long w;
+      if (!kw(v[t] + zero, k, w)) {
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
+      if (pass == 0 || (k >> hs) == (prefix >> hs)) atomicAdd(&sh.hist[(k >> shift) & dmask], w);
+      __builtin_amdgcn_sched_barrier(0);  // one element at a time: bounded register use
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 4l..4l+3; suffix sums from the top bin down
-      const unsigned long long b0 = sh.hist[4 * tid], b1 = sh.hist[4 * tid + 1],
-                               b2 = sh.hist[4 * tid + 2], b3 = sh.hist[4 * tid + 3];
-      const unsigned long long mine = b0 + b1 + b2 + b3;
-      // inclusive suffix scan over lanes (lane l gets the sum over lanes >= l)
-      unsigned long long suf = mine;
+    // thread tid owns bins 2tid, 2tid+1; suffix sums from the top bin down
+    const unsigned long long b0 = sh.hist[2 * tid], b1 = sh.hist[2 * tid + 1];
+    const unsigned long long mine = b0 + b1;
+    unsigned long long suf = mine;  // sum over lanes >= lane of this wave
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_down(suf, o, 64);
-        if (tid + o < 64) suf += y;
-      }
-      const unsigned long long after = suf - mine;  // lanes > l
-      // largest digit d with above + sum_{bins >= d} >= target
-      int d = -1;
-      const unsigned long long s3 = above + after + b3, s2 = s3 + b2, s1 = s2 + b1,
-                               s0 = s1 + b0;
-      if (s3 >= target) d = 4 * tid + 3;
-      else if (s2 >= target) d = 4 * tid + 2;
-      else if (s1 >= target) d = 4 * tid + 1;
-      else if (s0 >= target) d = 4 * tid;
-      // the largest lane with a hit holds the answer
-      const unsigned long long hit = __ballot(d >= 0);
-      const int hl = hit ? (63 - (int)__clzll(hit)) : -1;
-      if (tid == 0) sh.bcast_i[0] = hl;
-      if (hl >= 0 && tid == hl) {
-        // weight above the chosen digit = above + (sum of bins > d)
-        unsigned long long ab = above + after;
-        if (d < 4 * tid + 3) ab += b3;
-        if (d < 4 * tid + 2) ab += b2;
-        if (d < 4 * tid + 1) ab += b1;
-        sh.bcast_i[1] = d;
-        sh.bcast_ull = ab;
-      }
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long y = shfl_down_u64(suf, o);
+      if (lane + o < 64) suf += y;
     }
+    if (lane == 0) sh.wsuf[wv] = suf;
     __syncthreads();
-    if (sh.bcast_i[0] < 0) {
-      __syncthreads();
-      return 0u;  // nothing reaches the target: keep all
+    unsigned long long after = suf - mine;  // bins >= 2tid + 2
+    for (int i = wv + 1; i < NWV; ++i) after += sh.wsuf[i];
+    const unsigned long long n2 = above + after, n1 = n2 + b1, n0 = n1 + b0;
+    // the largest digit d whose weight at or above it (plus `above`) reaches the target
+    if (n1 >= target && n2 < target) {
+      sh.bcast_i[0] = 2 * tid + 1;
+      sh.bcast_ull[0] = n2;
+      sh.bcast_ull[1] = n1;
+    } else if (n0 >= target && n1 < target) {
+      sh.bcast_i[0] = 2 * tid;
+      sh.bcast_ull[0] = n1;
+      sh.bcast_ull[1] = n0;
     }
-    const int d = sh.bcast_i[1];
-    above = sh.bcast_ull;
+    if (pass == 0 && tid == 0) sh.bcast_ull[2] = n0;  // the total weight
+    __syncthreads();
+    const int d = sh.bcast_i[0];
+    if (d < 0) {  // first pass only: all elements together do not reach the target
+      const unsigned long long total = sh.bcast_ull[2];
+      __syncthreads();
+      return RadixResult{0u, total, true};
+    }
+    above = sh.bcast_ull[0];
+    kept = sh.bcast_ull[1];
     prefix |= ((uint32_t)d) << shift;
     __syncthreads();
   }
-  return prefix;
+  return RadixResult{prefix, kept, false};
 }
 
 // In place: v holds a logit row on entry (-inf past the row's end) and the processed
@@ -133,71 +193,91 @@ __device__ __forceinline__ uint32_t radix_select(const float (&v)[VPT], WeightF 
 template <int VPT>
 __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const SamplingKnobs& kn,
                                             VocabLDS& sh) {
-  const int tid = threadIdx.x;
-  if (tid == 0) sh.zero = 0.f;  // published by the barrier inside block_or
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) sh.zero = 0.f;  // published by the barrier below
+  // finiteness and the maximum in one block reduction
   int bad = 0;
+  float m = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < VPT; ++t)
+  for (int t = 0; t < VPT; ++t) {
     if (t * VT + tid < V && !isfinite(v[t])) bad = 1;
-  bad = block_or(bad, sh.ired);
+    m = fmaxf(m, v[t]);
+  }
+  m = wave_max_f(m);
+  const bool wbad = __ballot(bad) != 0ull;
+  if (lane == 0) {
+    sh.fred[wv] = m;
+    sh.ired[wv] = wbad;
+  }
+  __syncthreads();
+  m = -INFINITY;
+  bad = 0;
+  for (int i = 0; i < NWV; ++i) {
+    m = fmaxf(m, sh.fred[i]);
+    bad |= sh.ired[i];
+  }
   if (bad) {
 #pragma unroll
     for (int t = 0; t < VPT; ++t) v[t] = 0.f;
+    __syncthreads();
     return false;
   }
   // top-k on the logit (the order of l/T is the order of l for T > 0); dropped
-  // elements become -inf
+  // elements become -inf.  The maximum is always kept.
   if (kn.top_k > 0 && kn.top_k < V) {
-    const uint32_t tk = radix_select<VPT>(v, [](float) { return 1ull; },
-                                          (unsigned long long)kn.top_k, sh);
+    const RadixResult r = radix_select<VPT>(
+        v,
+        [](float x, uint32_t& k, unsigned long long& w) {
+          k = okey(x);
+          w = 1ull;
+          return x != -INFINITY;
+        },
+        (unsigned long long)kn.top_k, sh);
     const float zero = sh.zero;
 #pragma unroll
     for (int t = 0; t < VPT; ++t)
-      if (okey(v[t] + zero) < tk) v[t] = -INFINITY;
+      if (okey(v[t] + zero) < r.t) v[t] = -INFINITY;
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < VPT; ++t) m = fmaxf(m, v[t]);
-  m = block_max(m, sh.fred);
+  // e = exp((l - max) / T), once per element (0 for dropped and padding elements)
   const float it = kn.inv_t;
   double s = 0.0;
-  {
-    const float zero = sh.zero;
 #pragma unroll
-    for (int t = 0; t < VPT; ++t) {
-      s += (double)expf((v[t] + zero - m) * it);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int t = 0; t < VPT; ++t) {
+    v[t] = expf((v[t] - m) * it);
+    s += (double)v[t];
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const double S = block_sum(s, sh.dred);
+  const double S = block_sum_d(s, sh.dred);
   const double invS = 1.0 / S;
-  double S2 = 1.0;
+  double norm = invS;
+  uint32_t tkeep = 0u;  // keep e with bits >= tkeep (e >= 0: bit order is value order)
   if (kn.top_p < 1.0f) {
-    const double scale = 4503599627370496.0;  // 2^52
-    const unsigned long long target = (unsigned long long)((double)kn.top_p * scale);
-    const uint32_t tp = radix_select<VPT>(
+    // mass of element i: round(e_i / S * 2^52), from one fma (adding 2^52 leaves the
+    // rounded integer in the low mantissa bits; e_i / S <= 1 keeps it below 2^53)
+    const double ws = invS * 4503599627370496.0;  // 2^52 / S
+    const unsigned long long target =
+        (unsigned long long)((double)kn.top_p * 4503599627370496.0);
+    const RadixResult r = radix_select<VPT>(
         v,
-        [=](float x) {
-          const double p1 = (double)expf((x - m) * it) * invS;
-          return (unsigned long long)(p1 * scale + 0.5);
+        [=](float e, uint32_t& k, unsigned long long& w) {
+          k = __float_as_uint(e);  // e >= 0: the bit pattern is order-preserving
+          w = (unsigned long long)__double_as_longlong(
+                  __builtin_fma((double)e, ws, 4503599627370496.0)) -
+              0x4330000000000000ull;
+          return e > 0.f;
         },
         target, sh);
-    double s2 = 0.0;
-    const float zero = sh.zero;
-#pragma unroll
-    for (int t = 0; t < VPT; ++t) {
-      if (okey(v[t] + zero) < tp) v[t] = -INFINITY;
-      s2 += (double)expf((v[t] - m) * it) * invS;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    S2 = block_sum(s2, sh.dred);
+    tkeep = r.all ? 0u : r.t;
+    norm = ws / (double)r.kept;  // 1 / (kept sum of e), the kept sum from exact integers
   }
-  const double norm = invS / S2;
+  // e + zero (zero re-read from LDS) keeps the compiler from reusing the e pass's
+  // fp64 conversions, which would hold 2 * VPT registers across the top-p passes
   __syncthreads();
   const float zero = sh.zero;
 #pragma unroll
   for (int t = 0; t < VPT; ++t) {
-    v[t] = (float)((double)expf((v[t] + zero - m) * it) * norm);
+    const float e = __float_as_uint(v[t]) >= tkeep ? v[t] + zero : 0.f;
+    v[t] = (float)((double)e * norm);
     __builtin_amdgcn_sched_barrier(0);
   }
   return true;
@@ -207,11 +287,15 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
 // running sum exceeds u*S, S the total.  Running sums in fp64: thread c sums the 32
 // consecutive tokens of chunk c (in a rotated but fixed order, so LDS banks do not
 // collide), a block scan over the 1024 chunk sums locates the chunk holding the
-// crossing, and one thread walks that chunk in token order.  Returns -1 if S == 0.
+// crossing -- the one thread whose inclusive sum exceeds u*S while its predecessor's
+// does not -- and that thread's wave walks the chunk with a 32-lane prefix sum.
+// Returns -1 if S == 0.
 __device__ __forceinline__ int inverse_cdf_lds(int V, double u, VocabLDS& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   constexpr int CH = MAXVPT;  // tokens per chunk; chunk c = [c*CH, c*CH + CH)
-  __syncthreads();            // sh.w complete
+  constexpr int NONE = 0x7fffffff;
+  if (tid == 0) sh.bcast_i[2] = NONE;
+  __syncthreads();  // sh.w complete
   double c = 0.0;
   const int c0 = tid * CH;
   if (c0 < V) {
@@ -224,7 +308,7 @@ __device__ __forceinline__ int inverse_cdf_lds(int V, double u, VocabLDS& sh) {
   double inc = c;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o, 64);
+    const double y = shfl_up_d(inc, o);
     if (lane >= o) inc += y;
   }
   if (lane == 63) sh.scan[wv] = inc;
@@ -239,22 +323,40 @@ __device__ __forceinline__ int inverse_cdf_lds(int V, double u, VocabLDS& sh) {
     return -1;
   }
   const double T = u * S;
-  const int hit = block_min_int(inc > T ? tid : 0x7fffffff, sh.ired);
-  // the owner of the crossing chunk walks it (its exclusive prefix is inc - c)
-  if (hit != 0x7fffffff && tid == hit) {
-    double run = inc - c;
-    int tok = -1, last_pos = -1;
-    for (int e = 0; e < CH; ++e) {
-      const int i = c0 + e;
-      if (i >= V) break;
-      const float x = sh.w[i];
-      if (x > 0.f) last_pos = i;
-      run += (double)x;
-      if (run > T) { tok = i; break; }
+  // the predecessor's inclusive sum, as that thread holds it (the wave's offset is the
+  // previous wave's last inclusive sum: the same additions in the same order)
+  const double up = shfl_up_d(inc, 1);
+  const double prev = lane == 0 ? off : up;
+  // Exactly one owner when the running sums are monotone; should rounding in the
+  // scan tree ever break that, the smallest token found wins (atomicMin), which is the
+  // first owner's.
+  const bool owner = inc > T && prev <= T;
+  const unsigned long long ob = __ballot(owner);
+  if (ob) {
+    const int ol = __ffsll((long long)ob) - 1;
+    const int base = (wv * 64 + ol) * CH;
+    const double run = __longlong_as_double(
+        ((long long)__builtin_amdgcn_readlane((int)(__double_as_longlong(prev) >> 32), ol) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)__double_as_longlong(prev), ol));
+    const int i = base + lane;
+    const float x = (lane < CH && i < V) ? sh.w[i] : 0.f;
+    double ps = (double)x;  // inclusive prefix over lanes 0..lane
+#pragma unroll
+    for (int o = 1; o < CH; o <<= 1) {
+      const double y = shfl_up_d(ps, o);
+      if (lane >= o) ps += y;
     }
-    sh.bcast_i[2] = tok >= 0 ? tok : last_pos;
+    const unsigned long long crossed = __ballot(lane < CH && run + ps > T);
+    const unsigned long long pos = __ballot(x > 0.f);
+    if (lane == 0) {
+      int tok;
+      if (crossed) tok = base + __ffsll((long long)crossed) - 1;
+      else tok = pos ? base + 63 - __clzll(pos) : -1;  // rounding: last positive of the chunk
+      if (tok >= 0) atomicMin(&sh.bcast_i[2], tok);
+    }
   }
-  if (hit == 0x7fffffff && tid == 0) {
+  __syncthreads();
+  if (sh.bcast_i[2] == NONE && tid == 0) {
     // rounding put u*S at or past the end: the last token with positive weight
     int last_pos = -1;
     for (int i = V - 1; i >= 0; --i)
@@ -287,7 +389,8 @@ __device__ __forceinline__ void load_row(float (&v)[VPT], const float* row, int 
 }
 
 // One workgroup per (b, j), j = 0..K.  Writes res_acc[b*K + j] (j < K), res_cand[b*(K+1)+j]
-// and res_status[b*(K+1)+j].
+// and res_status[b*(K+1)+j].  While the draft row is processed, the processed target
+// row waits in the LDS weight buffer (one row in registers at a time).
 template <int VPT>
 __global__ __launch_bounds__(VT) void k_accept_rows(
     const float* __restrict__ p_logits, const float* __restrict__ q_logits,
@@ -299,20 +402,30 @@ __global__ __launch_bounds__(VT) void k_accept_rows(
   if (round_dev) round = *round_dev;
   const int b = blockIdx.x / (K + 1), j = blockIdx.x % (K + 1), tid = threadIdx.x;
   const bool has_q = j < K;
-  float pv[VPT], qv[VPT];
-  load_row<VPT>(pv, p_logits + ((size_t)b * (K + 1) + j) * V, V);
+  const float* prow = p_logits + ((size_t)b * (K + 1) + j) * V;
   int status = 0;
-  if (!process_row<VPT>(pv, V, kn, sh)) status |= SPEC_ROW_NONFINITE;
-  if (dbg_p) {
-    float* d = dbg_p + ((size_t)b * (K + 1) + j) * V;
-#pragma unroll
-    for (int t = 0; t < VPT; ++t)
-      if (t * VT + tid < V) d[t * VT + tid] = pv[t];
-  }
   int cand = -1;
-  if (has_q) {
+  {
+    float pv[VPT];
+    load_row<VPT>(pv, prow, V);
+    if (!process_row<VPT>(pv, V, kn, sh)) status |= SPEC_ROW_NONFINITE;
+    if (dbg_p) {
+      float* d = dbg_p + ((size_t)b * (K + 1) + j) * V;
+#pragma unroll
+      for (int t = 0; t < VPT; ++t)
+        if (t * VT + tid < V) d[t * VT + tid] = pv[t];
+    }
+    store_w<VPT>(pv, V, sh);  // P -> sh.w (the bonus row samples from it directly)
+  }
+  if (!has_q) {
+    if (!(status & SPEC_ROW_NONFINITE)) {
+      const double u = philox_uniform(seed, round, j, b, 2);
+      cand = inverse_cdf_lds(V, u, sh);
+    }
+  } else {
+    float qv[VPT];
     load_row<VPT>(qv, q_logits + ((size_t)b * K + j) * V, V);
-    if (!process_row<VPT>(qv, V, kn, sh)) status |= SPEC_ROW_NONFINITE;
+    if (!process_row<VPT>(qv, V, kn, sh)) status |= SPEC_ROW_NONFINITE;  // publishes sh.w
     if (dbg_q) {
       float* d = dbg_q + ((size_t)b * K + j) * V;
 #pragma unroll
@@ -326,9 +439,9 @@ __global__ __launch_bounds__(VT) void k_accept_rows(
     } else {
 #pragma unroll
       for (int t = 0; t < VPT; ++t)
-        if (t * VT + tid == x) { sh.px = pv[t]; sh.qx = qv[t]; }
+        if (t * VT + tid == x) sh.qx = qv[t];
       __syncthreads();
-      const float px = sh.px, qx = sh.qx;
+      const float px = sh.w[x], qx = sh.qx;
       if (qx == 0.f) status |= SPEC_ROW_Q_ZERO;
       const double u = philox_uniform(seed, round, j, b, 1);
       accept = (u * (double)qx < (double)px) ? 1 : 0;
@@ -336,21 +449,24 @@ __global__ __launch_bounds__(VT) void k_accept_rows(
     if (!(status & (SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN)) && !accept) {
       // residual max(0, p - q), kept in the q registers
 #pragma unroll
-      for (int t = 0; t < VPT; ++t) qv[t] = fmaxf(pv[t] - qv[t], 0.f);
+      for (int t = 0; t < VPT; ++t) {
+        const int i = t * VT + tid;
+        qv[t] = i < V ? fmaxf(sh.w[i] - qv[t], 0.f) : 0.f;
+      }
       const double u = philox_uniform(seed, round, j, b, 2);
       store_w<VPT>(qv, V, sh);
       cand = inverse_cdf_lds(V, u, sh);
       if (cand < 0) {
+        // empty residual (p <= q everywhere): sample P, processed again from its logits
         status |= SPEC_ROW_RESIDUAL_EMPTY;
+        float pv[VPT];
+        load_row<VPT>(pv, prow, V);
+        process_row<VPT>(pv, V, kn, sh);
         store_w<VPT>(pv, V, sh);
         cand = inverse_cdf_lds(V, u, sh);
       }
     }
     if (tid == 0) res_acc[b * K + j] = accept;
-  } else if (!(status & SPEC_ROW_NONFINITE)) {
-    const double u = philox_uniform(seed, round, j, b, 2);
-    store_w<VPT>(pv, V, sh);
-    cand = inverse_cdf_lds(V, u, sh);
   }
   if (tid == 0) {
     res_cand[b * (K + 1) + j] = cand;
