@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="7b", choices=["tiny", "small", "7b", "70b"])
+    ap.add_argument("--workload", default="7b", choices=["tiny", "small", "7b", "70b", "accept"],
+                    help="model workloads run full speculative rounds; 'accept' times the "
+                         "fused accept / resample step alone on synthetic logits")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--K", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
@@ -226,6 +228,71 @@ def verify_only(args, wl):
                       "kernel_sources_sha256": gemm_source_hash()}))
 
 
+def accept_only(args):
+    """The accept / resample step alone: target logits [B, K+1, V] ~ N(0, 2^2), draft
+    logits = target + N(0, 0.5^2), temperature 0.8, top-k and top-p off, draft tokens
+    drawn from the processed draft rows (input synthesis, outside the timed region).
+    A step is one spec_accept_resample call over the batch; the roofline is that of the
+    vocab kernel, which reads every logit row once."""
+    import torch
+
+    from speculative_decoding_forward_amd import binding, synth
+
+    B = args.batch or 32
+    K = args.K or 8
+    V = 32000
+    knobs = (0.8, 0, 1.0)
+    dev = "cuda"
+    p, q = synth.vocab_logits(args.seed, B, K, V, 2.0, 0.5)
+    P = torch.from_numpy(p).to(dev)
+    Q = torch.from_numpy(q).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    probs = torch.softmax(Q.double() / knobs[0], dim=-1).reshape(B * K, V)
+    X = torch.multinomial(probs, 1, generator=g).reshape(B, K).to(torch.int32).contiguous()
+    del probs
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    n_out = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = binding.accept_workspace(B, K)
+    for r in range(args.warmup):
+        binding.accept_resample(P, Q, X, knobs, args.seed, r, out, n_out, st, ws)
+    torch.cuda.synchronize()
+    n_sum = torch.zeros((B,), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        binding.accept_resample(P, Q, X, knobs, args.seed, args.warmup + i, out, n_out, st, ws)
+        b.record(stream)
+        n_sum += n_out
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    tokens = int(n_sum.sum().item())
+    assert int((st != 0).sum().item()) == 0
+    vb = (B * (K + 1) * V + B * K * V) * 4  # every logit row read once
+    c_med = float(np.median(call_ms))
+    achieved = vb / (c_med / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "accepted tokens/s + vocab-kernel HBM GB/s (% of peak), accept/resample alone",
+        "value": tokens / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: N(0,2^2) target logits, draft = target + N(0,0.5^2)",
+        "config": {"workload": "accept/resample alone", "batch": B, "K": K, "vocab": V,
+                   "temperature": knobs[0], "top_k": 0, "top_p": 1.0},
+        "call_ms_median": c_med,
+        "tokens_per_row_per_call": tokens / (B * args.steps),
+        "roofline": {"bound": "hbm", "kernel": "k_accept_rows + k_select (one call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_call": vb},
+    }))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +313,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+    if args.workload == "accept":
+        accept_only(args)
         return
     wl = synth.WORKLOADS[args.workload]
     if args.verify_only:

@@ -121,6 +121,21 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   auto compute = [&](int slot, int i) {
     const bool in_share = i < nmine;
     const int kb = (blk0 + AW * i) * AKB;  // first key position of the block
+    if (kb + AKB > len_end) {
+      // the block holding the row's end: positions from len_end on were never written
+      // by this row (the arena is caller memory), and P = 0 there does not cancel a
+      // NaN in the P V product, so those V elements are zeroed (K needs no care: masked
+      // scores are replaced, not multiplied)
+      typedef unsigned short u16x8v __attribute__((ext_vector_type(8)));
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        u16x8v w = __builtin_bit_cast(u16x8v, vf[slot][u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kb + (e < 4 ? 4 * g + e : 12 + 4 * g + e) >= len_end) w[e] = 0;
+        vf[slot][u] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
     float sc[2][4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {

@@ -110,6 +110,30 @@ def test_bf16_micro_ragged(kind, hd):
             assert np.abs(kd - ko).max() <= 2 ** -7 * max(1.0, np.abs(ko).max())
 
 
+@pytest.mark.parametrize("M", [1, 6])
+def test_unwritten_cache_positions_are_ignored(M):
+    """Positions at or past a row's length hold whatever the caller's arena held: with
+    the arena first filled with NaN bytes, a verify pass (one token, and K+1 = 6) gives
+    bitwise the logits and appended entries of the same pass over a zero-filled arena.
+    The context ends inside a 32-key block, so the last block read straddles the end."""
+    shape = bf16_micro("gelu", hd=128, d=512)
+    m, _ = setup(shape, seed=7)
+    B, max_len, n = 2, 160, 77
+    fill = synth.kv_fill(shape, B, max_len, n, seed=7, device=DEV)
+    new = synth.context_ids(8, B, M, shape.vocab)
+    res = []
+    for word in (0, -1):  # 0xFFFF is a NaN in bf16
+        kv = binding.KVCache(shape, B, max_len)
+        kv.data().view(torch.int16).fill_(word)  # the K/V elements only
+        kv.import_(fill[:, :, :, :, :n].contiguous())
+        kv.len.fill_(n)
+        g, st = gpu_forward(m, kv, new)
+        assert np.all(st == 0) and np.all(np.isfinite(g))
+        res.append((g, kv.export(n + M).float().cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
+
+
 def test_overflow_and_bad_tokens_flagged():
     shape = bf16_micro("swiglu")
     m, Wn = setup(shape, seed=4)
@@ -198,10 +222,12 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
     return g, o, spread, st
 
 
-@pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5)])
+@pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
+                                         ("small", 8, 7), ("7b", 8, 7)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
-    layers of the target."""
+    layers of the target.  64 rows (B=8, K=7) take the four-row-tile GEMM, the prefill
+    configuration, with paired column tiles where the tile count favours them."""
     g, o, spread, st = synthetic_kv_case(wl_name, B, K, layers=2)
     assert np.all(st == 0)
     assert_bf16_logits(g, o, spread, f"{wl_name} B={B} K={K} 2 layers")
