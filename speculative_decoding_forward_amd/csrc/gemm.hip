@@ -161,23 +161,26 @@ hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd,
 constexpr int SS_NP_MAX = 512;     // partial sums per row (d_model <= 8192)
 constexpr int ROPE_HALF_MAX = 64;  // rotation pairs per head (head_dim <= 128)
 
-// Dynamic LDS of the epilogue wave, sized per launch (epi_lds_bytes): partial sums of up
-// to 16 rows, RoPE factors of the block's rows (one row tile, QKV_ROPE), and the
-// residual values and gains of one tile (RESID).
+// Dynamic LDS of the epilogue wave, sized per launch (epi_lds_bytes): the partial sums
+// of squares of the block's rows (all of them, or 16 at a time when they do not fit),
+// and the inputs of the tile group being finished: RoPE factors (QKV_ROPE; with one row
+// tile those of every row, else the group's 8 pairs per tile) or residual values and
+// gains (RESID).  Everything is requested ahead of use by direct global-to-LDS loads.
 struct EpiLds {
-  float* ss;       // [min(16, rows)][np]
-  double2* rope;   // [rows][hd/2]
-  float* xres;     // [16][16]
-  float* gain;     // [16]
+  float* ss;       // [ss rows][np]
+  double2* rope;   // MT == 1: [rows][hd/2]; MT > 1: [NT][MT*16][8]
+  float* xres;     // [NT][MT*16][16]
+  float* gain;     // [NT][16]
 };
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline int epi_lds_bytes(int mt, int mode, int rows16, int np, int half,
-                                             int rows, bool norm_in) {
-  int b = norm_in ? align16(rows16 * np * 4) : 0;
-  if (mt == 1 && mode == EPI_QKV_ROPE) b += align16(rows * half * 16);
-  return b + 16 * 16 * 4 + 16 * 4;
+__host__ __device__ inline int epi_lds_bytes(int mt, int nt, int mode, int ss_rows, int np,
+                                             int half, int rows, bool norm_in) {
+  int b = norm_in ? align16(ss_rows * np * 4) : 0;
+  if (mode == EPI_QKV_ROPE) b += mt == 1 ? align16(rows * half * 16) : nt * mt * 16 * 8 * 16;
+  if (mode == EPI_RESID) b += nt * (mt * 16 * 16 * 4 + 16 * 4);
+  return b;
 }
 
 // Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` with direct loads: lane l
@@ -191,19 +194,40 @@ __device__ __forceinline__ void lds_copy(const void* src, void* dst, int bytes, 
   }
 }
 
-// Residual values x[r0 + row][16 t .. 16 t + 15] (rows < rows) and gains of tile t.
+// Residual values x[r0 + row][16 t .. 16 t + 15] (row < rows) and gains of tile t:
+// 16 rows per pass, four lanes per row.
 __device__ __forceinline__ void lds_copy_resid(const GemmArgs& g, int t, int r0, int rows,
                                                float* xres, float* gain, int lane) {
-  const int row = lane >> 2, q = lane & 3;
-  if (row < rows)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(g.x + (size_t)(r0 + row) * g.N + 16 * t +
-                                                        4 * q),
-        (__attribute__((address_space(3))) void*)xres, 16, 0, 0);
+  const int q = lane & 3;
+  for (int rb = 0; rb < rows; rb += 16) {
+    const int row = rb + (lane >> 2);
+    if (row < rows)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(g.x + (size_t)(r0 + row) * g.N +
+                                                          16 * t + 4 * q),
+          (__attribute__((address_space(3))) void*)(xres + rb * 16), 16, 0, 0);
+  }
   if (lane < 4)
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void*)(g.gain + 16 * t + 4 * lane),
         (__attribute__((address_space(3))) void*)gain, 16, 0, 0);
+}
+
+// RoPE factors of the 8 rotation pairs of QKV tile t (q and k sections) for rows
+// r0 .. r0 + rows - 1: [rows][8] (cos, sin), 8 rows per pass, 8 lanes per row.
+__device__ __forceinline__ void lds_copy_rope_tile(const GemmArgs& g, int t, int r0, int rows,
+                                                   double2* rope, int lane) {
+  const QkvTile qt = qkv_tile(t, g.d, g.hd);
+  if (qt.sec >= 2) return;
+  const int half = g.hd >> 1, j = lane & 7;
+  for (int rb = 0; rb < rows; rb += 8) {
+    const int row = rb + (lane >> 3);
+    if (row < rows)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(g.rope_rows +
+                                                          ((size_t)(r0 + row) * half + qt.i0 + j) * 2),
+          (__attribute__((address_space(3))) void*)(rope + rb * 8), 16, 0, 0);
+  }
 }
 
 // Wait for this wave's outstanding global loads, direct-to-LDS ones included.
@@ -257,7 +281,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
   if (mode == EPI_RESID) {
     // residual update, next input bf16(x * g) and the tile's sums of squares per row
     const int col = 16 * t + nl, np = g.N >> 4;
-    const float gc = MT == 1 ? L.gain[nl] : g.gain[col];
+    const float gc = L.gain[nl];
 #pragma unroll 1
     for (int mt = 0; mt < MT; ++mt) {
       const floatx4 v = sum_partials<MT>(part, mt, lane);
@@ -267,7 +291,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
         const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
         float xn = 0.f;
         if (r < R) {
-          const float xo = MT == 1 ? L.xres[rr * 16 + nl] : g.x[(size_t)r * g.N + col];
+          const float xo = L.xres[rr * 16 + nl];
           xn = xo + v[e];
           g.x[(size_t)r * g.N + col] = xn;
           g.h_out[(size_t)r * g.N + col] = f32_to_bf16(xn * gc);
@@ -309,12 +333,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
         u16 o;
         if (qt.sec < 2) {
           // rotation of the pair (i, i + hd/2) at the row's position, in fp64
-          double2 c2;
-          if constexpr (MT == 1) {
-            c2 = L.rope[rr * half + i];
-          } else {
-            c2 = *reinterpret_cast<const double2*>(g.rope_rows + ((size_t)r * half + i) * 2);
-          }
+          const double2 c2 = MT == 1 ? L.rope[rr * half + i] : L.rope[rr * 8 + (nl & 7)];
           const float lo = is_hi ? yp : y, hi = is_hi ? y : yp;
           o = is_hi ? f32_to_bf16((float)((double)hi * c2.x + (double)lo * c2.y))
                     : f32_to_bf16((float)((double)lo * c2.x - (double)hi * c2.y));
@@ -405,30 +424,50 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     const int rows = min(MT * 16, g.R - r0);  // >= 1
     const int np = g.ss_np, half = g.hd >> 1;
     EpiLds L;
+    const int ss_rows = min(g.ss_rows, g.R);  // partial-sum rows the LDS holds at once
     {
       char* p = reinterpret_cast<char*>(epi_dyn);
       L.ss = reinterpret_cast<float*>(p);
-      if (g.ss_in) p += align16(min(16, g.R) * np * 4);
+      if (g.ss_in) p += align16(ss_rows * np * 4);
       L.rope = reinterpret_cast<double2*>(p);
-      if (MT == 1 && g.mode == EPI_QKV_ROPE) p += align16(g.R * half * 16);
+      if (g.mode == EPI_QKV_ROPE) p += MT == 1 ? align16(g.R * half * 16) : NT * MT * 16 * 8 * 16;
       L.xres = reinterpret_cast<float*>(p);
-      L.gain = L.xres + 256;
+      L.gain = L.xres + NT * MT * 16 * 16;
     }
-    // requests first: direct-to-LDS copies of the row factors' partial sums and the
-    // first tile's inputs, then the row bookkeeping
-    if (g.ss_in) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, min(16, rows) * np * 4, lane);
-    if constexpr (MT == 1) {
-      if (g.mode == EPI_QKV_ROPE)
-        lds_copy(g.rope_rows + (size_t)r0 * half * 2, L.rope, rows * half * 16, lane);
-      else if (g.mode == EPI_RESID)
-        lds_copy_resid(g, bx, r0, rows, L.xres, L.gain, lane);
-    }
+    // the inputs of tile group `grp` into the per-tile slots (RESID; QKV_ROPE with
+    // several row tiles -- one row tile keeps every row's factors from the start)
+    auto stage_group = [&](int grp) {
+#pragma unroll 1
+      for (int n = 0; n < NT; ++n) {
+        const int t = grp * NT + n;
+        if (g.mode == EPI_RESID)
+          lds_copy_resid(g, t, r0, rows, L.xres + n * MT * 16 * 16, L.gain + n * 16, lane);
+        else if (MT > 1 && g.mode == EPI_QKV_ROPE)
+          lds_copy_rope_tile(g, t, r0, rows, L.rope + n * MT * 16 * 8, lane);
+      }
+    };
+    // requests first: the rows' token counts and start positions, direct-to-LDS copies of
+    // the row factors' partial sums and the first group's inputs
     int ntok[(MT * 16 + 63) / 64], p0v[(MT * 16 + 63) / 64];
 #pragma unroll
     for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
       const int r = min(r0 + lane + 64 * k, g.R - 1), b = qdiv(r, g.M);
       ntok[k] = g.ntok_eff ? g.ntok_eff[b] : g.M;
       p0v[k] = g.pos0 ? g.pos0[b] : 0;
+    }
+    const bool ss_all = ss_rows >= rows;
+    if (g.ss_in)
+      lds_copy(g.ss_in + (size_t)r0 * np, L.ss, (ss_all ? rows : min(16, rows)) * np * 4, lane);
+    if (MT == 1 && g.mode == EPI_QKV_ROPE)
+      lds_copy(g.rope_rows + (size_t)r0 * half * 2, L.rope, rows * half * 16, lane);
+    stage_group(bx);
+    if constexpr (MT > 1) {
+      // Several row tiles: the streaming waves' A requests are then many, and a request
+      // queued behind them returns after 5-20 us; the streaming waves start once these
+      // are on their way (the matching barrier opens their code).
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
@@ -443,31 +482,39 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     wait_vm();
     if (g.ss_in) {
       for (int rb = 0; rb < MT && 16 * rb < rows; ++rb) {
-        if (rb > 0) {  // later 16-row batches (MT > 1)
+        const float* src = L.ss + (ss_all ? rb * 16 * np : 0);
+        if (!ss_all && rb > 0) {  // 16 rows at a time: the next batch (requested late)
           wave_lds_sync();
           lds_copy(g.ss_in + (size_t)(r0 + 16 * rb) * np, L.ss, min(16, rows - 16 * rb) * np * 4,
                    lane);
           wait_vm();
         }
-        row_factors(L.ss, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
+        row_factors(src, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
       }
     }
     wave_lds_sync();
     for (int ct = 0; ct < nt; ++ct) {
       epi_barrier();
 #pragma unroll 1
-      for (int n = 0; n < NT; ++n)
+      for (int n = 0; n < NT; ++n) {
+        EpiLds Ln = L;
+        if (MT > 1) Ln.rope = L.rope + n * MT * 16 * 8;
+        Ln.xres = L.xres + n * MT * 16 * 16;
+        Ln.gain = L.gain + n * 16;
         gemm_tile_epilogue<MT>(g, (bx + ct * G) * NT + n, r0, part[ct & 1][n], rowinfo, rowscale,
-                               L, lane);
-      if constexpr (MT == 1) {
-        if (g.mode == EPI_RESID && ct + 1 < nt) {
-          wave_lds_sync();
-          lds_copy_resid(g, bx + (ct + 1) * G, r0, rows, L.xres, L.gain, lane);
-          wait_vm();
-        }
+                               Ln, lane);
+      }
+      if (ct + 1 < nt && (g.mode == EPI_RESID || (MT > 1 && g.mode == EPI_QKV_ROPE))) {
+        wave_lds_sync();  // this group's slots are read
+        stage_group(bx + (ct + 1) * G);
+        wait_vm();
       }
     }
     return;
+  }
+  if constexpr (MT > 1) {
+    __builtin_amdgcn_s_barrier();  // the epilogue wave's requests go first
+    __builtin_amdgcn_sched_barrier(0);
   }
   const int nl = lane & 15, gq = lane >> 4;
   const int R = g.R, nsuper = g.K >> 7;
@@ -645,8 +692,16 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
-  const unsigned lds = (unsigned)epi_lds_bytes(mt, g.mode, std::min(16, g.R), g.ss_np, g.hd / 2,
-                                               g.R, g.ss_in != nullptr);
+  // stage every row's partial sums of squares at once when the LDS holds them next to
+  // the tile partials (static LDS of the kernel), else 16 rows at a time
+  const int static_lds = 2 * NTc * GW * mt * 1024 + mt * 16 * (8 + 8);
+  g.ss_rows = mt * 16;
+  if (static_lds + epi_lds_bytes(mt, NTc, g.mode, std::min(g.ss_rows, g.R), g.ss_np, g.hd / 2,
+                                 g.R, g.ss_in != nullptr) > 160 * 1024)
+    g.ss_rows = 16;
+  const unsigned lds = (unsigned)epi_lds_bytes(mt, NTc, g.mode, std::min(g.ss_rows, g.R),
+                                               g.ss_np, g.hd / 2, g.R, g.ss_in != nullptr);
+  if (static_lds + (int)lds > 160 * 1024) return hipErrorInvalidValue;
 #define SPEC_GEMM_LAUNCH(MT_, NT_, GY)                                                     \
   hipExtLaunchKernelGGL(k_gemm_bf16<MT_, NT_>, dim3(G, GY), dim3(GT), lds, s, e0, e1, 0, g)
   if (tiles <= 1) {

@@ -80,6 +80,7 @@ struct GemmArgs {
   const float* ss_in;
   int ss_np;
   float eps;
+  int ss_rows;  // rows of ss_in the epilogue stages in LDS at once (set by the launcher)
   // RESID: x [R, N] += Y; h_out [R, N] = bf16(x * gain) (the next normalised product's
   // input) and ss_out [R][N/16] its partial sums of squares per 16-column tile
   float* x;

@@ -223,7 +223,7 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
-                                         ("small", 8, 7), ("7b", 8, 7)])
+                                         ("small", 8, 7), ("7b", 8, 7), ("70b", 1, 4)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
     layers of the target.  64 rows (B=8, K=7) take the four-row-tile GEMM, the prefill
