@@ -610,6 +610,209 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   }
 }
 
+// K-outer variant for several row tiles (R > 16) and several tiles per workgroup.
+// Workgroup bx owns the tiles bx + G j (j < per, G = gridDim.x) and takes them in chunks
+// of TPW.  Each streaming wave walks its K super-steps once per chunk; per step it loads
+// the A fragments of all row tiles once and multiplies them into every tile of the chunk
+// (accumulators in registers), so A is requested once per step instead of once per tile
+// and step -- at 48 rows the loads per tile and step fall from 10-16 to 4 + 12/TPW, and
+// load instructions, not bytes, bound the tile-at-a-time kernel there.  The partials meet
+// in LDS at the end of a chunk and all five waves share the chunk's epilogues.  Every
+// output element accumulates its K steps in the same order as in k_gemm_bf16 (the same
+// per-wave step sequence, waves summed in order), so results are bitwise the same.
+// Tiles past the end are computed on the last tile (in bounds) and dropped.
+// (register budget: TPW accumulators + two steps of A fragments + two of W, 256 VGPRs;
+// with four row tiles the A fragments alone take half of it, so that case stays on
+// k_gemm_bf16)
+template <int MT> constexpr int ko_tpw_max() { return MT == 2 ? 8 : 5; }
+
+template <int MT, int TPW>
+__global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
+  static_assert((MT == 2 || MT == 3) && TPW >= 2 && TPW <= ko_tpw_max<MT>(), "K-outer shape");
+  __shared__ floatx4 part[TPW][GW][MT][64];
+  __shared__ int2 rowinfo[MT * 16];
+  __shared__ double rowscale[MT * 16];
+  extern __shared__ float4 epi_dyn[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int bx = blockIdx.x, G = gridDim.x;
+  const int r0 = blockIdx.y * (MT * 16);
+  const int rows = min(MT * 16, g.R - r0);  // >= 1
+  const int np = g.ss_np;
+  EpiLds L;
+  {
+    char* p = reinterpret_cast<char*>(epi_dyn);
+    L.ss = reinterpret_cast<float*>(p);
+    if (g.ss_in) p += align16(16 * np * 4);
+    L.rope = reinterpret_cast<double2*>(p);
+    if (g.mode == EPI_QKV_ROPE) p += TPW * MT * 16 * 8 * 16;
+    L.xres = reinterpret_cast<float*>(p);
+    L.gain = L.xres + TPW * MT * 16 * 16;
+  }
+  const int nchunks = (per + TPW - 1) / TPW;
+  auto tile_of = [&](int c, int j) { return min(bx + G * (c * TPW + j), g.ntiles - 1); };
+  auto stage_chunk = [&](int c) {
+#pragma unroll 1
+    for (int j = 0; j < TPW; ++j) {
+      const int t = tile_of(c, j);
+      if (g.mode == EPI_RESID)
+        lds_copy_resid(g, t, r0, rows, L.xres + j * MT * 16 * 16, L.gain + j * 16, lane);
+      else if (g.mode == EPI_QKV_ROPE)
+        lds_copy_rope_tile(g, t, r0, rows, L.rope + j * MT * 16 * 8, lane);
+    }
+  };
+  // streaming state
+  const int nl = lane & 15, gq = lane >> 4;
+  const int nsuper = g.K >> 7;
+  const int S = (nsuper + GW - 1) / GW;  // steps per wave
+  const size_t tile_elems = (size_t)nsuper * 2048;
+
+#pragma unroll 1
+  for (int c = 0; c < nchunks; ++c) {
+    if (wv == GW) {
+      if (c == 0) {
+        // requests first: counts and start positions, the first 16 rows' sums of squares,
+        // the chunk's epilogue inputs; then the streaming waves start
+        int ntok[(MT * 16 + 63) / 64], p0v[(MT * 16 + 63) / 64];
+#pragma unroll
+        for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
+          const int r = min(r0 + lane + 64 * k, g.R - 1), b = qdiv(r, g.M);
+          ntok[k] = g.ntok_eff ? g.ntok_eff[b] : g.M;
+          p0v[k] = g.pos0 ? g.pos0[b] : 0;
+        }
+        if (g.ss_in) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, min(16, rows) * np * 4, lane);
+        stage_chunk(0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
+          const int rr = lane + 64 * k, r = r0 + rr;
+          int2 info{0, 0};
+          if (r < g.R) {
+            const int j = r - qdiv(r, g.M) * g.M, pos = p0v[k] + j;
+            info = int2{pos, (j < ntok[k] ? 1 : 0) | (j < ntok[k] && pos < g.max_len ? 2 : 0)};
+          }
+          if (rr < MT * 16) rowinfo[rr] = info;
+        }
+        wait_vm();
+        if (g.ss_in) {
+          // later 16-row batches are requested behind the weight stream; the results are
+          // needed only at the end of the chunk
+          for (int rb = 0; rb < MT && 16 * rb < rows; ++rb) {
+            if (rb > 0) {
+              wave_lds_sync();
+              lds_copy(g.ss_in + (size_t)(r0 + 16 * rb) * np, L.ss,
+                       min(16, rows - 16 * rb) * np * 4, lane);
+              wait_vm();
+            }
+            row_factors(L.ss, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
+          }
+        }
+      } else {
+        stage_chunk(c);
+        wait_vm();
+      }
+    } else {
+      if (c == 0) {
+        __builtin_amdgcn_s_barrier();  // the epilogue wave's requests go first
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      floatx4 acc[TPW][MT];
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 af[2][MT][4];
+      bf16x8 wf[2][4];
+      // Buffer loads: a 32-bit lane offset and a scalar step / tile offset per request,
+      // and requests past the buffer's end read zeros, so rows past R and steps past the
+      // wave's last one need no selects (steps past the last re-read an in-bounds weight
+      // segment and pair it with zero A fragments).
+      const int wvu = __builtin_amdgcn_readfirstlane(wv);
+      const bool wactu = wvu < nsuper;
+      const int lastu = wactu ? (nsuper - 1 - wvu) / GW : 0;
+      const uint32_t a_bytes = (uint32_t)g.R * (uint32_t)g.lda * 2u;
+      const __amdgpu_buffer_rsrc_t ra = coherent_rsrc(g.A, a_bytes);
+      const __amdgpu_buffer_rsrc_t rw = coherent_rsrc(g.W, (size_t)g.ntiles * tile_elems * 2);
+      uint32_t aoff[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = r0 + mt * 16 + nl;
+        aoff[mt] = r < g.R ? ((uint32_t)r * (uint32_t)g.lda + 8u * gq) * 2u : a_bytes;
+      }
+      const uint32_t woff = 16u * lane;
+      uint32_t wtile[TPW];  // byte offset of each tile of the chunk (uniform)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) wtile[j] = (uint32_t)tile_of(c, j) * (uint32_t)tile_elems * 2u;
+      auto loadA = [&](int buf, int i) {
+        const uint32_t so = (wactu && i <= lastu) ? (uint32_t)(wvu + i * GW) * 256u : a_bytes;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            af[buf][mt][s] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mt] + 64u * s, so, 0));
+      };
+      auto loadW = [&](int buf, int i, int j) {
+        const uint32_t js = wactu ? (uint32_t)(wvu + (i <= lastu ? i : lastu) * GW) : 0u;
+        const uint32_t so = wtile[j] + js * 4096u;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          wf[buf][s] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 1024u * s, so, 2));
+      };
+      loadA(0, 0);
+      loadW(0, 0, 0);
+      // two steps per round so both register buffers are addressed statically
+      for (int i0 = 0; i0 < S; i0 += 2) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = i0 + ii;
+          loadA((ii + 1) & 1, i + 1);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const int f = ii * TPW + j;
+            if (j + 1 < TPW) loadW((f + 1) & 1, i, j + 1);
+            else loadW((f + 1) & 1, i + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ii & 1][mt][s],
+                                                                     wf[f & 1][s], acc[j][mt],
+                                                                     0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) part[j][wv][mt][lane] = acc[j][mt];
+    }
+    __syncthreads();  // partials, row factors and the chunk's staged inputs are complete
+#pragma unroll 1
+    for (int j = wv; j < TPW; j += GW + 1) {
+      const int t = bx + G * (c * TPW + j);
+      if (t >= g.ntiles) break;
+      EpiLds Lj = L;
+      Lj.rope = L.rope + j * MT * 16 * 8;
+      Lj.xres = L.xres + j * MT * 16 * 16;
+      Lj.gain = L.gain + j * 16;
+      gemm_tile_epilogue<MT>(g, t, r0, part[j], rowinfo, rowscale, Lj, lane);
+    }
+    __syncthreads();  // the chunk's partials and input slots may be reused
+  }
+}
+
+__host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode, int np, bool norm_in) {
+  int b = norm_in ? align16(16 * np * 4) : 0;
+  if (mode == EPI_QKV_ROPE) b += tpw * mt * 16 * 8 * 16;
+  if (mode == EPI_RESID) b += tpw * (mt * 16 * 16 * 4 + 16 * 4);
+  return b;
+}
+
 // ------------------------------------------------------------------ fp32 path -----
 
 // fp32: one wave per output column n, lanes stride K; rows looped.
@@ -673,6 +876,27 @@ int device_cus() {
 // Grid: G persistent workgroups per row block, at most one per compute unit, G chosen
 // so that the tiles divide as evenly as possible (every workgroup gets ceil(tiles / G)
 // or one fewer).
+template <int MT, int TPW>
+static void launch_ko_one(dim3 grid, unsigned lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                          const GemmArgs& g, int per) {
+  if constexpr (TPW <= ko_tpw_max<MT>())  // the dispatcher never asks for more
+    hipExtLaunchKernelGGL(k_gemm_bf16_ko<MT, TPW>, grid, dim3(GT), lds, s, e0, e1, 0, g, per);
+}
+
+template <int MT>
+static void launch_ko(int tpw, dim3 grid, unsigned lds, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1, const GemmArgs& g, int per) {
+  switch (tpw) {
+    case 2: launch_ko_one<MT, 2>(grid, lds, s, e0, e1, g, per); break;
+    case 3: launch_ko_one<MT, 3>(grid, lds, s, e0, e1, g, per); break;
+    case 4: launch_ko_one<MT, 4>(grid, lds, s, e0, e1, g, per); break;
+    case 5: launch_ko_one<MT, 5>(grid, lds, s, e0, e1, g, per); break;
+    case 6: launch_ko_one<MT, 6>(grid, lds, s, e0, e1, g, per); break;
+    case 7: launch_ko_one<MT, 7>(grid, lds, s, e0, e1, g, per); break;
+    default: launch_ko_one<MT, 8>(grid, lds, s, e0, e1, g, per); break;
+  }
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   GemmArgs g = g0;
   g.ntiles = gemm_blocks_x(g);
@@ -692,6 +916,24 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
+  {
+    // two or three row tiles and several tiles per workgroup: the K-outer kernel, in
+    // chunks of at most ko_tpw_max tiles of equal size
+    const int kper = cdiv(g.ntiles, gmax);
+    if ((mt == 2 || mt == 3) && kper >= 2) {
+      const int tmax = mt == 2 ? ko_tpw_max<2>() : ko_tpw_max<3>();
+      const int tpw = cdiv(kper, cdiv(kper, tmax));
+      const int kG = cdiv(g.ntiles, kper);
+      const int kstatic = tpw * GW * mt * 1024 + mt * 16 * (8 + 8);
+      const int kdyn = ko_lds_bytes(mt, tpw, g.mode, g.ss_np, g.ss_in != nullptr);
+      if (kstatic + kdyn <= 160 * 1024) {
+        const dim3 grid(kG, rowblocks);
+        if (mt == 2) launch_ko<2>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
+        else launch_ko<3>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
+        return hipGetLastError();
+      }
+    }
+  }
   // stage every row's partial sums of squares at once when the LDS holds them next to
   // the tile partials (static LDS of the kernel), else 16 rows at a time
   const int static_lds = 2 * NTc * GW * mt * 1024 + mt * 16 * (8 + 8);
