@@ -50,7 +50,9 @@ def build(verbose=False, jobs=None):
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs]
+    # every symbol must resolve at link time (a kernel whose stub was not emitted would
+    # otherwise only show up when the library is loaded)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -230,6 +230,14 @@ __device__ __forceinline__ void lds_copy_rope_tile(const GemmArgs& g, int t, int
   }
 }
 
+// 16 bytes per lane from a buffer (byte offset voff + soff; zeros past its end) straight
+// to LDS at lds + 16 * lane.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
 // Wait for this wave's outstanding global loads, direct-to-LDS ones included.
 __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -621,15 +629,18 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
 // output element accumulates its K steps in the same order as in k_gemm_bf16 (the same
 // per-wave step sequence, waves summed in order), so results are bitwise the same.
 // Tiles past the end are computed on the last tile (in bounds) and dropped.
-// (register budget: TPW accumulators + two steps of A fragments + two of W, 256 VGPRs;
-// with four row tiles the A fragments alone take half of it, so that case stays on
-// k_gemm_bf16)
-template <int MT> constexpr int ko_tpw_max() { return MT == 2 ? 8 : 5; }
+// (register budget, 256 VGPRs: TPW accumulators, one step of A fragments -- the next
+// step's wait in LDS -- and two steps of W)
+template <int MT> constexpr int ko_tpw_max() { return MT == 4 ? 5 : 8; }
 
 template <int MT, int TPW>
 __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
-  static_assert((MT == 2 || MT == 3) && TPW >= 2 && TPW <= ko_tpw_max<MT>(), "K-outer shape");
-  __shared__ floatx4 part[TPW][GW][MT][64];
+  static_assert(MT >= 2 && MT <= 4 && TPW >= 2 && TPW <= ko_tpw_max<MT>(), "K-outer shape");
+  // the chunk's partials; while the chunk streams, the same LDS holds each streaming
+  // wave's A staging slot ([GW][MT][4][64] 16-byte fragments, at most TPW >= 4 times
+  // smaller than the partials, hence the max)
+  constexpr int PT = TPW > 4 ? TPW : 4;
+  __shared__ floatx4 part[PT][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
   __shared__ double rowscale[MT * 16];
   extern __shared__ float4 epi_dyn[];
@@ -722,12 +733,13 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
       for (int j = 0; j < TPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[j][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 af[2][MT][4];
+      bf16x8 af[MT][4];
       bf16x8 wf[2][4];
       // Buffer loads: a 32-bit lane offset and a scalar step / tile offset per request,
       // and requests past the buffer's end read zeros, so rows past R and steps past the
       // wave's last one need no selects (steps past the last re-read an in-bounds weight
-      // segment and pair it with zero A fragments).
+      // segment and pair it with zero A fragments).  The next step's A fragments go
+      // straight to this wave's LDS slot and are read into registers at the step's start.
       const int wvu = __builtin_amdgcn_readfirstlane(wv);
       const bool wactu = wvu < nsuper;
       const int lastu = wactu ? (nsuper - 1 - wvu) / GW : 0;
@@ -744,14 +756,22 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
       uint32_t wtile[TPW];  // byte offset of each tile of the chunk (uniform)
 #pragma unroll
       for (int j = 0; j < TPW; ++j) wtile[j] = (uint32_t)tile_of(c, j) * (uint32_t)tile_elems * 2u;
-      auto loadA = [&](int buf, int i) {
+      char* aslot = reinterpret_cast<char*>(&part[0][0][0][0]) + (size_t)wvu * MT * 4 * 1024;
+      auto dmaA = [&](int i) {
         const uint32_t so = (wactu && i <= lastu) ? (uint32_t)(wvu + i * GW) * 256u : a_bytes;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            af[buf][mt][s] = __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mt] + 64u * s, so, 0));
+            buffer_to_lds16(ra, aslot + (mt * 4 + s) * 1024, aoff[mt] + 64u * s, so);
+      };
+      auto readA = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            af[mt][s] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(aslot + (mt * 4 + s) * 1024 + 16 * lane));
       };
       auto loadW = [&](int buf, int i, int j) {
         const uint32_t js = wactu ? (uint32_t)(wvu + (i <= lastu ? i : lastu) * GW) : 0u;
@@ -761,14 +781,21 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
           wf[buf][s] = __builtin_bit_cast(
               bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 1024u * s, so, 2));
       };
-      loadA(0, 0);
+      dmaA(0);
       loadW(0, 0, 0);
-      // two steps per round so both register buffers are addressed statically
+      // two steps per round so both W register buffers are addressed statically
       for (int i0 = 0; i0 < S; i0 += 2) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
           const int i = i0 + ii;
-          loadA((ii + 1) & 1, i + 1);
+          // step i's A is in the slot once only the last W request (4 loads, issued after
+          // it) may still be outstanding; reading it frees the slot for step i + 1
+          __builtin_amdgcn_sched_barrier(0);
+          __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          readA();
+          __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          dmaA(i + 1);
 #pragma unroll
           for (int j = 0; j < TPW; ++j) {
             const int f = ii * TPW + j;
@@ -779,18 +806,22 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
               for (int s = 0; s < 4; ++s)
-                acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ii & 1][mt][s],
-                                                                     wf[f & 1][s], acc[j][mt],
-                                                                     0, 0, 0);
+                acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt][s], wf[f & 1][s],
+                                                                     acc[j][mt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      // the partials overwrite the A slots: every wave's requests have landed and every
+      // wave is past its last read of its slot
+      wait_vm();
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) part[j][wv][mt][lane] = acc[j][mt];
     }
+    if (wv == GW) __builtin_amdgcn_s_barrier();  // the streaming waves' slot barrier
     __syncthreads();  // partials, row factors and the chunk's staged inputs are complete
 #pragma unroll 1
     for (int j = wv; j < TPW; j += GW + 1) {
@@ -917,19 +948,21 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
   {
-    // two or three row tiles and several tiles per workgroup: the K-outer kernel, in
-    // chunks of at most ko_tpw_max tiles of equal size
+    // several row tiles and several tiles per workgroup: the K-outer kernel, in chunks
+    // of equal size, at most ko_tpw_max tiles and as many as its LDS allows
     const int kper = cdiv(g.ntiles, gmax);
-    if ((mt == 2 || mt == 3) && kper >= 2) {
-      const int tmax = mt == 2 ? ko_tpw_max<2>() : ko_tpw_max<3>();
-      const int tpw = cdiv(kper, cdiv(kper, tmax));
-      const int kG = cdiv(g.ntiles, kper);
-      const int kstatic = tpw * GW * mt * 1024 + mt * 16 * (8 + 8);
-      const int kdyn = ko_lds_bytes(mt, tpw, g.mode, g.ss_np, g.ss_in != nullptr);
-      if (kstatic + kdyn <= 160 * 1024) {
+    if (mt >= 2 && kper >= 2) {
+      const int tmax = mt == 4 ? ko_tpw_max<4>() : ko_tpw_max<2>();
+      for (int tcap = tmax; tcap >= 2; --tcap) {
+        const int tpw = cdiv(kper, cdiv(kper, tcap));
+        const int kG = cdiv(g.ntiles, kper);
+        const int kstatic = std::max(tpw, 4) * GW * mt * 1024 + mt * 16 * (8 + 8);
+        const int kdyn = ko_lds_bytes(mt, tpw, g.mode, g.ss_np, g.ss_in != nullptr);
+        if (kstatic + kdyn > 160 * 1024) continue;
         const dim3 grid(kG, rowblocks);
         if (mt == 2) launch_ko<2>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
-        else launch_ko<3>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
+        else if (mt == 3) launch_ko<3>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
+        else launch_ko<4>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
         return hipGetLastError();
       }
     }
