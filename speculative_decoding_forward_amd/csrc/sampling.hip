@@ -113,13 +113,13 @@ struct RadixResult {
 };
 
 // Largest key t such that the total weight of the participating elements with key
-// >= t reaches `target` (> 0).  kw(x, key, weight) says whether element x takes part
-// and gives its key and integer weight.  Three passes over 11-, 11- and 10-bit digits
+// >= t reaches `target` (> 0).  kf(x, key) says whether element x takes part and gives
+// its key; wf(x) its integer weight (evaluated only for elements a pass counts).  Three passes over 11-, 11- and 10-bit digits
 // (high to low), each an LDS histogram of the elements whose key matches the digits
 // chosen so far, a block-wide suffix scan over the 2048 bins, and the unique bin
 // where the running weight crosses the target.
-template <int VPT, typename KW>
-__device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KW kw,
+template <int VPT, typename KF, typename WF>
+__device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KF kf, WF wf,
                                                     unsigned long long target, VocabLDS& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t prefix = 0;
@@ -137,13 +137,10 @@ __device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KW kw
     const float zero = sh.zero;
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
+      const float x = v[t] + zero;
       uint32_t k;
-      unsigned long long w;
-      if (!kw(v[t] + zero, k, w)) {
-        __builtin_amdgcn_sched_barrier(0);
-        continue;
-      }
-      if (pass == 0 || (k >> hs) == (prefix >> hs)) atomicAdd(&sh.hist[(k >> shift) & dmask], w);
+      if (kf(x, k) && (pass == 0 || (k >> hs) == (prefix >> hs)))
+        atomicAdd(&sh.hist[(k >> shift) & dmask], wf(x));
       __builtin_amdgcn_sched_barrier(0);  // one element at a time: bounded register use
     }
     __syncthreads();
@@ -159,7 +156,14 @@ __device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KW kw
     if (lane == 0) sh.wsuf[wv] = suf;
     __syncthreads();
     unsigned long long after = suf - mine;  // bins >= 2tid + 2
-    for (int i = wv + 1; i < NWV; ++i) after += sh.wsuf[i];
+#pragma unroll 1
+    for (int i0 = wv + 1; i0 < NWV; i0 += 4) {  // later waves' totals, four reads at a time
+      unsigned long long y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = i0 + k < NWV ? sh.wsuf[i0 + k] : 0ull;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) after += y[k];
+    }
     const unsigned long long n2 = above + after, n1 = n2 + b1, n0 = n1 + b0;
     // the largest digit d whose weight at or above it (plus `above`) reaches the target
     if (n1 >= target && n2 < target) {
@@ -227,12 +231,11 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
   if (kn.top_k > 0 && kn.top_k < V) {
     const RadixResult r = radix_select<VPT>(
         v,
-        [](float x, uint32_t& k, unsigned long long& w) {
+        [](float x, uint32_t& k) {
           k = okey(x);
-          w = 1ull;
           return x != -INFINITY;
         },
-        (unsigned long long)kn.top_k, sh);
+        [](float) { return 1ull; }, (unsigned long long)kn.top_k, sh);
     const float zero = sh.zero;
 #pragma unroll
     for (int t = 0; t < VPT; ++t)
@@ -259,12 +262,14 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
         (unsigned long long)((double)kn.top_p * 4503599627370496.0);
     const RadixResult r = radix_select<VPT>(
         v,
-        [=](float e, uint32_t& k, unsigned long long& w) {
+        [](float e, uint32_t& k) {
           k = __float_as_uint(e);  // e >= 0: the bit pattern is order-preserving
-          w = (unsigned long long)__double_as_longlong(
-                  __builtin_fma((double)e, ws, 4503599627370496.0)) -
-              0x4330000000000000ull;
           return e > 0.f;
+        },
+        [=](float e) {
+          return (unsigned long long)__double_as_longlong(
+                     __builtin_fma((double)e, ws, 4503599627370496.0)) -
+                 0x4330000000000000ull;
         },
         target, sh);
     tkeep = r.all ? 0u : r.t;
@@ -299,9 +304,17 @@ __device__ __forceinline__ int inverse_cdf_lds(int V, double u, VocabLDS& sh) {
   double c = 0.0;
   const int c0 = tid * CH;
   if (c0 < V) {
-    for (int e = 0; e < CH; ++e) {
-      const int i = c0 + ((e + tid) & (CH - 1));
-      if (i < V) c += (double)sh.w[i];
+#pragma unroll
+    for (int e0 = 0; e0 < CH; e0 += 8) {  // 8 independent reads, then their additions in order
+      float xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = c0 + ((e0 + e + tid) & (CH - 1));
+        xs[e] = i < V ? sh.w[i] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c += (double)xs[e];
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // inclusive block scan of the chunk sums
