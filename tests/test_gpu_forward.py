@@ -223,11 +223,13 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
-                                         ("small", 8, 7), ("7b", 8, 7), ("70b", 1, 4)])
+                                         ("small", 8, 7), ("7b", 8, 7), ("7b", 8, 3),
+                                         ("7b", 5, 6), ("70b", 1, 4)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
-    layers of the target.  64 rows (B=8, K=7) take the four-row-tile GEMM, the prefill
-    configuration, with paired column tiles where the tile count favours them."""
+    layers of the target.  Rows 6 and 5 take the one-row-tile GEMM; 32, 35 (a ragged last
+    row tile), 48 and 64 rows the K-outer GEMM with two to four row tiles where a
+    workgroup owns several column tiles, else the tile-at-a-time one."""
     g, o, spread, st = synthetic_kv_case(wl_name, B, K, layers=2)
     assert np.all(st == 0)
     assert_bf16_logits(g, o, spread, f"{wl_name} B={B} K={K} 2 layers")
@@ -240,13 +242,14 @@ def test_full_depth_small():
     assert_bf16_logits(g, o, spread, "small 24 layers")
 
 
-@pytest.mark.parametrize("wl_name,B", [("small", 1), ("7b", 1), ("7b", 8)])
-def test_verify_equals_single_token_calls_bitwise(wl_name, B):
+@pytest.mark.parametrize("wl_name,B,K", [("small", 1, None), ("7b", 1, None), ("7b", 8, None),
+                                         ("7b", 8, 3)])
+def test_verify_equals_single_token_calls_bitwise(wl_name, B, K):
     """At full size: one call over K+1 positions gives bitwise the logits of K+1
     one-token calls (the premise of the verify pass), and the appended cache entries
     are bitwise equal; repeating the call is bitwise deterministic."""
     wl = synth.WORKLOADS[wl_name]
-    K = wl.K
+    K = K or wl.K
     shape = wl.target
     m, _ = (binding.Model(shape, synth.make_weights(shape, seed=0, device=DEV)), None)
     max_len = wl.ctx + K + 1
