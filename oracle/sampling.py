@@ -40,6 +40,13 @@ Readings of points the pages leave open (each is listed in the design notes):
   * inverse CDF: smallest i with C_i > u*S, C the running sum in token-id order,
     S = C_{V-1}.  An empty residual (S = 0 after a rejection) falls back to sampling P_a.
   * temperature and top_p are float32 parameters: their float32 values are used.
+  * T = 0 is argmax decoding ([LENS] "How much faster in practice?", the argmax column of
+    Table 2, and the practice notes contrasting temperature 0 with 1; [NOTE]
+    Recommendation R3 names greedy decoding as the other mode): every processed row is
+    one-hot at the largest logit, the lowest token id among equal largest logits.  The
+    largest logit survives every top-k and top-p cut, so those knobs change nothing at
+    T = 0.  With one-hot rows the rule itself is unchanged: the draft proposes argmax q,
+    a draft is accepted iff it is argmax p, and the resample and bonus are argmax p.
 """
 import numpy as np
 
@@ -59,6 +66,7 @@ def f32(x):
 def transform(logits, temperature, top_k=0, top_p=1.0):
     """Processed probability row (float64) from one logit row.
 
+    0. T = 0: one-hot at the first index holding the largest logit (argmax decoding).
     1. z = logits / T                          (T > 0, float32 value)
     2. top-k (0 < k < V): z_i -> -inf where z_i < (k-th largest z); ties kept.
     3. s = exp(z - max z) / sum(exp(z - max z)).
@@ -67,6 +75,11 @@ def transform(logits, temperature, top_k=0, top_p=1.0):
     """
     T = f32(temperature)
     tp = f32(top_p)
+    if T == 0.0:
+        l = np.asarray(logits, dtype=np.float64)
+        s = np.zeros(l.size)
+        s[int(np.argmax(l))] = 1.0  # numpy's argmax returns the first maximal index
+        return s
     z = np.asarray(logits, dtype=np.float64) / T
     V = z.size
     if 0 < top_k < V:

@@ -61,3 +61,33 @@ def test_tiny_rounds_invariants_and_cache_consistency(tiny_weights):
         dn = model.forward(wl.draft, Wd, cd, pend)
         dfresh = model.forward(wl.draft, Wd, model.KVCache(wl.draft, 1, 256), committed[None])
         np.testing.assert_allclose(dn[0, -1], dfresh[0, -1], rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("draft_is_target", [False, True])
+def test_greedy_rounds_emit_the_targets_own_argmax_decoding(tiny_weights, draft_is_target):
+    """At T = 0 the method changes no output: whatever the draft proposes, the committed
+    tokens equal the target's own one-token-at-a-time argmax decoding (the argmax column
+    of the speedup table in [LENS] "How much faster in practice?" compares against exactly
+    that).  A slip in the accept test, the resample or the cache roll-back changes the
+    sequence."""
+    wl = tiny()
+    Wt, Wd = tiny_weights
+    B, n_rounds = 2, 6
+    ctx = synth.context_ids(3, B, wl.ctx, wl.target.vocab)
+    dshape, dW = (wl.target, Wt) if draft_is_target else (wl.draft, Wd)
+    st = rounds.SpecRows(wl.target, Wt, dshape, dW, ctx, wl.K, max_len=256,
+                         temperature=0.0, seed=0)
+    for _ in range(n_rounds):
+        toks, n_out, a, status = st.step()
+        assert np.all(status == 0)
+        if draft_is_target:
+            assert np.all(n_out == wl.K + 1)
+    for b in range(B):
+        new = st.tokens[b][wl.ctx:]
+        cache = model.KVCache(wl.target, 1, 256)
+        lg = model.forward(wl.target, Wt, cache, ctx[b:b + 1])
+        ref = []
+        while len(ref) < len(new):
+            ref.append(int(np.argmax(lg[0, -1].astype(np.float32))))
+            lg = model.forward(wl.target, Wt, cache, np.array([[ref[-1]]]))
+        assert new == ref

@@ -32,6 +32,54 @@ def test_transform_temperature(T):
                                rtol=1e-12)
 
 
+@pytest.mark.parametrize("knobs", [dict(), dict(top_k=5), dict(top_p=0.9), dict(top_k=3, top_p=0.5)])
+def test_greedy_is_the_zero_temperature_limit(knobs):
+    """T = 0 (argmax decoding) is the T -> 0 limit of the softmax path: once T is small
+    against the gap between the two largest logits, exp((l - max) / T) underflows to
+    exactly 0 for every other token, so the ordinary T > 0 path already returns the
+    one-hot row -- with or without top-k / top-p."""
+    rng = np.random.default_rng(2)
+    for _ in range(6):
+        l = rng.normal(0, 2, 300).astype(np.float32)
+        top2 = np.sort(l.astype(np.float64))[-2:]
+        T = (top2[1] - top2[0]) / 1000.0   # exp(-1000) is 0 in float64
+        lim = sampling.transform(l, T, **knobs)
+        assert np.count_nonzero(lim) == 1
+        assert np.array_equal(lim, sampling.transform(l, 0.0, **knobs))
+
+
+def test_greedy_ties_take_the_lowest_id():
+    """Equal largest logits: the lowest token id (the reading for argmax decoding)."""
+    l = np.array([0.5, 3.0, -1.0, 3.0, 3.0], np.float32)
+    assert np.array_equal(sampling.transform(l, 0.0), [0, 1, 0, 0, 0])
+    assert np.array_equal(sampling.transform(l[::-1].copy(), 0.0), [1, 0, 0, 0, 0])
+
+
+def test_greedy_rule_keeps_the_target_argmax_prefix():
+    """With one-hot rows the unchanged rule keeps the drafts up to the first one that is
+    not argmax p, then emits argmax p there (or the bonus argmax p_K): checked against a
+    direct comparison walk on random logits, with drafts that agree and disagree."""
+    rng = np.random.default_rng(3)
+    V, K = 50, 6
+    for trial in range(200):
+        pl = rng.normal(0, 1, (K + 1, V)).astype(np.float32)
+        ql = rng.normal(0, 1, (K, V)).astype(np.float32)
+        amax_p = pl.argmax(axis=1)
+        n_agree = rng.integers(0, K + 1)
+        xt = np.where(np.arange(K) < n_agree, amax_p[:K], rng.integers(0, V, K))
+        u_acc, u_res = rng.random(K), rng.random(K + 1)
+        toks, n, a, st = sampling.accept_resample_logits(pl, ql, xt, u_acc, u_res, 0.0)
+        walk = []
+        for j in range(K):
+            if xt[j] != amax_p[j]:
+                walk.append(int(amax_p[j]))
+                break
+            walk.append(int(xt[j]))
+        else:
+            walk.append(int(amax_p[K]))
+        assert toks == walk and n == len(walk)
+
+
 def _brute_top_k(l, k):
     # kept iff fewer than k tokens are strictly larger
     keep = np.array([np.sum(l > v) < k for v in l])
