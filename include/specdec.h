@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
   SPEC_OK = 0,
   SPEC_E_INVALID = -1,      /* null pointer, bad shape, bad knob value              */
-  SPEC_E_UNSUPPORTED = -2,  /* valid but not built: e.g. T = 0, V > 32768, no gfx950 */
+  SPEC_E_UNSUPPORTED = -2,  /* valid but not built: e.g. V > 32768, no gfx950 */
   SPEC_E_CAPACITY = -3,     /* workspace or arena smaller than the size query says  */
   SPEC_E_HIP = -4           /* a HIP launch failed; see spec_last_hip_error()        */
 } spec_status;
@@ -76,7 +76,10 @@ typedef struct {
 
 /* Sampling knobs applied to BOTH p and q before the rule ([NOTE] "Key results",
  * robust-to-knobs item, and Recommendation R3), in the order temperature -> top-k ->
- * top-p -> renormalise.  temperature > 0 (0 = greedy is not built: SPEC_E_UNSUPPORTED);
+ * top-p -> renormalise.  temperature >= 0; 0 is argmax decoding ([LENS] "How much faster
+ * in practice?", the argmax column of Table 2): each processed row is one-hot at the
+ * lowest token id holding the largest logit, top_k and top_p change nothing, and the rule
+ * emits the target's own argmax continuation;
  * top_k = 0 means off (0 <= top_k); top_p = 1 means off (0 < top_p <= 1).  Ties at a
  * top-k or top-p threshold are all kept. */
 typedef struct {

@@ -84,7 +84,8 @@ bool knobs_valid(const spec_sampling* k) {
 }
 
 SamplingKnobs to_knobs(const spec_sampling* k) {
-  return SamplingKnobs{1.0f / k->temperature, k->top_k, k->top_p};
+  const bool greedy = k->temperature == 0.f;
+  return SamplingKnobs{greedy ? 0.f : 1.0f / k->temperature, k->top_k, k->top_p, greedy ? 1 : 0};
 }
 
 // Workspace of the forward: regions carved from the caller's buffer.
@@ -692,7 +693,6 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
     return SPEC_E_INVALID;
   if (step == 0 && (!in_tok || !n_in)) return SPEC_E_INVALID;
   if (!kv_matches(draft, dkv)) return SPEC_E_INVALID;
-  if (knobs->temperature == 0.f) return SPEC_E_UNSUPPORTED;
   if (draft->cfg.vocab > 32768) return SPEC_E_UNSUPPORTED;
   if (((uintptr_t)ws) % 256) return SPEC_E_INVALID;
   const int M = step == 0 ? 2 : 1;
@@ -737,7 +737,6 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
   if ((pending == nullptr) != (n_pending == nullptr)) return SPEC_E_INVALID;
   if (tkv && tkv->batch < B) return SPEC_E_INVALID;
   if (dkv && dkv->batch < B) return SPEC_E_INVALID;
-  if (knobs->temperature == 0.f) return SPEC_E_UNSUPPORTED;
   if (V > 32768) return SPEC_E_UNSUPPORTED;
   if (ws_bytes < spec_accept_workspace_bytes(B, K)) return SPEC_E_CAPACITY;
   char* p = (char*)ws;

@@ -40,9 +40,10 @@ struct spec_kv {
 };
 
 struct SamplingKnobs {
-  float inv_t;
+  float inv_t;  // 1 / temperature (unused when greedy)
   int top_k;
   float top_p;
+  int greedy;   // temperature 0: argmax decoding
 };
 
 // kernel launchers (defined in the .hip files)

@@ -23,8 +23,12 @@
 // is deterministic: top-k on the key of the logit (ties are equal logits), top-p on
 // the key of the unnormalised probability e = exp((l - max) / T) with each element's
 // mass e/S as a 2^-52 fixed-point integer (ties are equal probabilities, the rule
-// "keep every token whose probability reaches the threshold's").
+// "keep every token whose probability reaches the threshold's").  Temperature 0 is
+// argmax decoding: the processed row is one-hot at the lowest index holding the
+// largest logit, and the rule then runs unchanged (the draft proposes argmax q, a
+// draft is accepted iff it is argmax p, the resample and the bonus are argmax p).
 #include <float.h>
+#include <limits.h>
 
 #include "common.h"
 #include "internal.h"
@@ -77,6 +81,12 @@ __device__ __forceinline__ double shfl_up_d(double v, int o) {
 // value of lane + o (wrapped; callers mask)
 __device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int o) {
   return shfl_src_u64(v, (lane_fresh() + o) & 63);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+    v = min(v, __builtin_amdgcn_ds_bpermute((lane_fresh() ^ o) << 2, v));
+  return v;
 }
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
@@ -225,6 +235,23 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
     for (int t = 0; t < VPT; ++t) v[t] = 0.f;
     __syncthreads();
     return false;
+  }
+  if (kn.greedy) {
+    // T = 0, argmax decoding: one-hot at the lowest index holding the maximum (the
+    // maximum survives any top-k or top-p cut, so those knobs change nothing here)
+    int first = INT_MAX;
+#pragma unroll
+    for (int t = VPT - 1; t >= 0; --t)
+      if (t * VT + tid < V && v[t] == m) first = t * VT + tid;
+    first = wave_min_i(first);
+    __syncthreads();  // every thread has read sh.ired above
+    if (lane == 0) sh.ired[wv] = first;
+    __syncthreads();
+    first = INT_MAX;
+    for (int i = 0; i < NWV; ++i) first = min(first, sh.ired[i]);
+#pragma unroll
+    for (int t = 0; t < VPT; ++t) v[t] = t * VT + tid == first ? 1.f : 0.f;
+    return true;
   }
   // top-k on the logit (the order of l/T is the order of l for T > 0); dropped
   // elements become -inf.  The maximum is always kept.

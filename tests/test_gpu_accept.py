@@ -89,12 +89,55 @@ def test_status_rows():
     assert g["status"][0] == 0 and 1 <= g["n_out"][0] <= K + 1
 
 
+@pytest.mark.parametrize("B,K,V,knobs", [
+    (8, 5, 32000, (0.0, 0, 0.95)),          # 7B-shape knobs at T = 0 (top-p inert)
+    (6, 4, 1029, (0.0, 7, 1.0)),            # ragged tail, top-k inert
+    (4, 16, 17, (0.0, 0, 1.0)),             # tiny vocabulary, largest K
+    (2, 2, 32768, (0.0, 0, 1.0)),           # largest vocabulary
+])
+def test_greedy_bit_exact(B, K, V, knobs):
+    """T = 0 (argmax decoding): every decision is an exact comparison of the same fp32
+    logits on both sides, so the processed rows (one-hot), accept flags, candidates,
+    outputs and status equal the oracle's bit for bit.  Row b agrees with the target
+    for its first b % (K + 1) positions (q = p there, so argmax q = argmax p), and every
+    row carries a planted tie at its maximum, placed before or after the first maximum."""
+    rng = np.random.default_rng(V + K)
+    p, q = synth.vocab_logits(B * 7 + V, B, K, V)
+    for b in range(B):
+        for j in range(K + 1):
+            i = int(rng.integers(0, V))
+            p[b, j, i] = p[b, j].max()
+            if j < K:
+                i = int(rng.integers(0, V))
+                q[b, j, i] = q[b, j].max()
+        n_agree = b % (K + 1)
+        q[b, :n_agree] = p[b, :n_agree]
+    xt = q.argmax(axis=2)                    # the greedy draft: argmax q, lowest id
+    g = gpu_accept(p, q, xt, knobs, seed=3, rnd=1)
+    T, k, tp = knobs
+    for b in range(B):
+        P = np.stack([sampling.transform(r, T, k, tp) for r in p[b]])
+        Q = np.stack([sampling.transform(r, T, k, tp) for r in q[b]])
+        assert np.array_equal(g["pp"][b], P) and np.array_equal(g["qp"][b], Q)
+        ua = philox.uniform(3, 1, np.arange(K), b, 1)
+        ur = philox.uniform(3, 1, np.arange(K + 1), b, 2)
+        toks, n, a, st = sampling.accept_resample_logits(p[b], q[b], xt[b], ua, ur, T, k, tp)
+        assert a >= b % (K + 1)
+        assert g["n_out"][b] == n and list(g["out"][b, :n]) == toks, (b, g["out"][b], toks)
+        assert np.all(g["out"][b, n:] == -1) and g["status"][b] == st == 0
+        amax = p[b].argmax(axis=1)
+        assert np.array_equal(g["acc"][b], (xt[b] == amax[:K]).astype(g["acc"].dtype))
+        for j in range(K + 1):
+            want = -1 if (j < K and xt[b, j] == amax[j]) else amax[j]
+            assert g["cand"][b, j] == want, (b, j)
+
+
 def test_argument_errors():
     B, K, V = 2, 2, 64
     p, q, xt = case(B, K, V, (1.0, 0, 1.0))
     with pytest.raises(binding.SpecError) as e:
-        gpu_accept(p, q, xt, (0.0, 0, 1.0), 0, 0)
-    assert e.value.status == binding.SPEC_E_UNSUPPORTED
+        gpu_accept(p, q, xt, (-0.5, 0, 1.0), 0, 0)
+    assert e.value.status == binding.SPEC_E_INVALID
     with pytest.raises(binding.SpecError) as e:
         gpu_accept(p, q, xt, (1.0, 0, 1.5), 0, 0)
     assert e.value.status == binding.SPEC_E_INVALID
