@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_verify_7b_b1_k5_traffic.md")
 GEMM_SOURCES = ["speculative_decoding_forward_amd/csrc/gemm.hip",
                 "speculative_decoding_forward_amd/csrc/common.h",
-                "speculative_decoding_forward_amd/csrc/internal.h"]
+                "speculative_decoding_forward_amd/csrc/gemm.h",
+                "speculative_decoding_forward_amd/csrc/kv_layout.h"]
 
 
 def parse():
@@ -296,6 +297,44 @@ def accept_only(args):
     }))
 
 
+AR_STEPS = 8  # single-token steps per graph of the plain-decoding baseline
+
+
+def ar_ms_per_token(binding, torch, model, kv, ws, B, V, knobs, seed, tok0, n_rep):
+    """Plain autoregressive decoding on the same kernels: a graph of AR_STEPS one-token
+    steps of `model` (forward + sample, the draft-step entry point) that rolls the cache
+    back at its end, replayed n_rep times between HIP events; returns the median ms per
+    token step.  Step 0 runs at two rows (room for two pending tokens), the rest at one."""
+    i32 = dict(dtype=torch.int32, device="cuda")
+    xt = torch.zeros((B, AR_STEPS), **i32)
+    ql = torch.zeros((B, AR_STEPS, V), dtype=torch.float32, device="cuda")
+    n_in = torch.ones(B, **i32)
+    saved = kv.len.clone()
+
+    def body():
+        for j in range(AR_STEPS):
+            binding.draft_step(model, kv, tok0, n_in, j, knobs, seed, 0, xt, ql, ws)
+        kv.rollback(saved)
+
+    body()  # eager pass: code loading, outside the measurement
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_rep)]
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.len, saved)
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) / AR_STEPS
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -332,7 +371,7 @@ def main():
     Wt = synth.make_weights(wl.target, seed=args.seed, model_id=synth.TARGET, device=dev)
     Wd = synth.make_weights(wl.draft, seed=args.seed, model_id=synth.DRAFT, device=dev)
     rounds_total = args.warmup + 1 + args.steps  # eager warm-up, graph warm-up, timed
-    max_len = wl.ctx + (rounds_total + 1) * (K + 1) + 2
+    max_len = wl.ctx + (rounds_total + 1) * (K + 1) + 2 + AR_STEPS
     dec = rounds.SpecDecoder(wl.target, Wt, wl.draft, Wd, B, K, max_len, knobs, seed=args.seed)
     ctx = synth.context_ids(args.seed, B, wl.ctx, wl.target.vocab)
     dec.prefill(ctx)
@@ -349,20 +388,24 @@ def main():
     # one round -- within the cache's capacity -- runs before the clock starts, with the
     # token accumulation of the timed loop: the first use of a kernel loads its code
     # (the accumulation's took 20-80 ms), which is not part of a round
-    n_out_sum = torch.zeros(B, dtype=torch.int64, device=dev)
+    # (per-round counts land in row i of n_hist: one elementwise add per round, as a
+    # running sum would cost)
+    n_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
     dec.replay()
-    n_out_sum += dec.n_out
-    n_out_sum.zero_()
+    n_hist[0] += dec.n_out
+    n_hist.zero_()
     len_start = dec.tkv.len.cpu().numpy().astype(np.float64)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         dec.replay()
-        n_out_sum += dec.n_out
+        n_hist[i] += dec.n_out
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    tokens = int(n_out_sum.sum().item())
+    hist = n_hist.cpu().numpy().astype(np.int64)
+    assert hist.min() >= 1, "a row emitted nothing (row status set)"
+    tokens = int(hist.sum())
     len_end = dec.tkv.len.cpu().numpy().astype(np.float64)
 
     # verify-pass latency: a graph of [verify-input assembly, verify pass, roll-back to
@@ -406,8 +449,33 @@ def main():
     achieved = gemm_avg_bytes / gemm_avg_s / 1e9
     vb = verify_bytes(wl.target, B, K, (len_start + len_end) / 2)
     v_med = float(np.median(verify_ms))
-    accepted = tokens - B * args.steps
-    alpha_hat = accepted / (B * args.steps * K)
+    # acceptance rate as the pages define it: the probability that a draft passes, given
+    # that every earlier one did ([LENS] §3.1: beta per position, alpha its expectation,
+    # i.i.d. in the tokens-per-run formula), estimated as accepted / (accepted +
+    # rejections); a round with all K accepted has no rejection
+    acc_counts = hist - 1
+    accepted = int(acc_counts.sum())
+    rejections = int((acc_counts < K).sum())
+    alpha_hat = accepted / max(1, accepted + rejections)
+    e_tokens_iid = (1 - alpha_hat ** (K + 1)) / (1 - alpha_hat) if alpha_hat < 1 else K + 1
+
+    # plain decoding on the same kernels: the target's and the draft's one-token steps
+    tok0 = torch.full((B, 2), -1, dtype=torch.int32, device=dev)
+    tok0[:, 0] = dec.pending[:, 0]
+    n_ar = max(6, min(args.steps, 20))
+    t_ar = ar_ms_per_token(binding, torch, dec.target, dec.tkv, dec.ws_t, B, wl.target.vocab,
+                           knobs, args.seed, tok0, n_ar)
+    d_ar = ar_ms_per_token(binding, torch, dec.draft, dec.dkv, dec.ws_d, B, wl.target.vocab,
+                           knobs, args.seed, tok0, n_ar)
+    c_hat = d_ar / t_ar
+    ar_tps = B / (t_ar / 1e3)
+    round_s = wall / args.steps
+    # the pages' expected wall-time improvement ([LENS] "How much faster in practice?",
+    # [ZSM] "How much faster"): tokens per run over the cost of K draft runs + one
+    # target run, in units of a target run
+    formula = e_tokens_iid / (K * c_hat + 1)
+    ar_bytes = verify_bytes(wl.target, B, 0, len_end)  # one token per row, weights once
+    e08 = (1 - 0.8 ** (K + 1)) / (1 - 0.8)
     res = {
         "metric": "accepted tokens/s + verify-pass HBM GB/s (% of peak), 7B-shape bf16, K=5",
         "value": tokens / wall,
@@ -435,6 +503,23 @@ def main():
         "verify_bytes": vb,
         "tokens_per_round_per_row": tokens / (B * args.steps),
         "alpha_measured": alpha_hat,
+        "tokens_per_round_at_alpha_iid": e_tokens_iid,
+        "autoregressive": {
+            "what": "plain decoding on the same kernels: one-token target steps (forward + "
+                    "sample), graph of 8 steps, median of HIP-event-timed replays",
+            "target_ms_per_token": t_ar, "tokens_per_s": ar_tps,
+            "draft_ms_per_token": d_ar, "c_measured": c_hat,
+            "speedup_measured": (tokens / wall) / ar_tps,
+            "speedup_formula_at_measured_alpha_c": formula,
+            "bandwidth_ceiling_tokens_per_s": B * HBM_PEAK_GBS * 1e9 / ar_bytes,
+            "bytes_per_token_step": ar_bytes,
+        },
+        "projected_at_alpha_0.8": {
+            "note": "context, not measured: the measured round time with the tokens per "
+                    "round that alpha = 0.8 would give",
+            "tokens_per_s": B * e08 / round_s,
+            "speedup_vs_measured_autoregressive": B * e08 / round_s / ar_tps,
+        },
         "verify_attention_ms": attn_ms / n_meas,
         "verify_gemm_ms": gemm_ms / n_meas,
         "roofline": {"bound": "hbm",

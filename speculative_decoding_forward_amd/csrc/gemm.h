@@ -1,0 +1,62 @@
+// Argument block and launchers of the weight GEMMs (defined in gemm.hip).  The GEMM
+// kernels compile from gemm.hip, this header and common.h alone.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specdec {
+
+// fused bf16 GEMM epilogues
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_GELU = 4 };
+
+struct GemmArgs {
+  const uint16_t* A;  // [R, K] bf16 activations
+  int lda;
+  const uint16_t* W;  // packed column tiles (see the packed layout in gemm.hip)
+  int N1;             // SWIGLU: gate/up width F (output row stride); else N
+  int R, N, K, mode;
+  int ntiles;  // column tiles (set by the launcher)
+  float* C;  // STORE: logits [R, N]; RESID: Y [R, N], added to the residual stream later
+  int ldc;
+  const int32_t* ntok_eff;  // [B] tokens per sequence (rows past it are padding)
+  int M;                    // rows per sequence
+  // QKV_ROPE
+  const int32_t* pos0;
+  int d, hd;
+  const double* rope_rows;  // [R][hd/2][2] (cos, sin) of each row's rotation angles
+  uint16_t* q_out;
+  uint16_t* kc;
+  uint16_t* vc;
+  size_t row_stride, head_stride;
+  int max_len;
+  // SWIGLU / GELU
+  uint16_t* act_out;
+  const uint16_t* zeros;  // >= 16 zero bytes (device)
+  // RMS-normalised input (QKV_ROPE, SWIGLU, GELU, STORE): A = bf16(x * g) of the rows and
+  // ss_in [R][ss_np] the partial sums of x^2 over 16-column groups; the product row r is
+  // scaled by 1 / sqrt(sum_p ss_in[r][p] / K + eps).  NULL: no scaling.
+  const float* ss_in;
+  int ss_np;
+  float eps;
+  int ss_rows;  // rows of ss_in the epilogue stages in LDS at once (set by the launcher)
+  // RESID: x [R, N] += Y; h_out [R, N] = bf16(x * gain) (the next normalised product's
+  // input) and ss_out [R][N/16] its partial sums of squares per 16-column tile
+  float* x;
+  const float* gain;
+  uint16_t* h_out;
+  float* ss_out;
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };
+hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
+                            uint16_t* dst, hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
+                           int N, int K, float* C, int accumulate, const float* rowscale,
+                           const int32_t* ntok_eff, int M, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1);
+int device_cus();  // compute units of the device
+
+}  // namespace specdec

@@ -42,7 +42,8 @@
 #include <math.h>
 
 #include "common.h"
-#include "internal.h"
+#include "gemm.h"
+#include "kv_layout.h"
 
 namespace specdec {
 

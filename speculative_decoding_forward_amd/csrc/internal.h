@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include "../../include/specdec.h"
+#include "gemm.h"
+#include "kv_layout.h"
 
 struct spec_model {
   spec_model_cfg cfg;
@@ -49,55 +51,6 @@ struct SamplingKnobs {
 // kernel launchers (defined in the .hip files)
 namespace specdec {
 
-// fused bf16 GEMM epilogues
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_GELU = 4 };
-
-struct GemmArgs {
-  const uint16_t* A;  // [R, K] bf16 activations
-  int lda;
-  const uint16_t* W;  // packed column tiles (see the packed layout in gemm.hip)
-  int N1;             // SWIGLU: gate/up width F (output row stride); else N
-  int R, N, K, mode;
-  int ntiles;  // column tiles (set by the launcher)
-  float* C;  // STORE: logits [R, N]; RESID: Y [R, N], added to the residual stream later
-  int ldc;
-  const int32_t* ntok_eff;  // [B] tokens per sequence (rows past it are padding)
-  int M;                    // rows per sequence
-  // QKV_ROPE
-  const int32_t* pos0;
-  int d, hd;
-  const double* rope_rows;  // [R][hd/2][2] (cos, sin) of each row's rotation angles
-  uint16_t* q_out;
-  uint16_t* kc;
-  uint16_t* vc;
-  size_t row_stride, head_stride;
-  int max_len;
-  // SWIGLU / GELU
-  uint16_t* act_out;
-  const uint16_t* zeros;  // >= 16 zero bytes (device)
-  // RMS-normalised input (QKV_ROPE, SWIGLU, GELU, STORE): A = bf16(x * g) of the rows and
-  // ss_in [R][ss_np] the partial sums of x^2 over 16-column groups; the product row r is
-  // scaled by 1 / sqrt(sum_p ss_in[r][p] / K + eps).  NULL: no scaling.
-  const float* ss_in;
-  int ss_np;
-  float eps;
-  int ss_rows;  // rows of ss_in the epilogue stages in LDS at once (set by the launcher)
-  // RESID: x [R, N] += Y; h_out [R, N] = bf16(x * gain) (the next normalised product's
-  // input) and ss_out [R][N/16] its partial sums of squares per 16-column tile
-  float* x;
-  const float* gain;
-  uint16_t* h_out;
-  float* ss_out;
-};
-
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };
-hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
-                            uint16_t* dst, hipStream_t s);
-hipError_t launch_gemm_f32(const float* A, const float* W, const float* W2, int N1, int R,
-                           int N, int K, float* C, int accumulate, const float* rowscale,
-                           const int32_t* ntok_eff, int M, hipStream_t s, hipEvent_t e0,
-                           hipEvent_t e1);
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
                              const float* g, float* x, void* h, float* ss, const double* rope,
                              const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
@@ -111,23 +64,10 @@ constexpr int kAttnMaxCUs = 1024;                     // bound on the CUs a spli
 int attn_nsplit(int B, int H, int M, int max_len);  // splits per (row, head, group)
 int attn_max_splits(int B, int H, int M, int max_len);  // bound of attn_nsplit (workspace)
 int attn_groups(int M);                               // query groups per row
-int device_cus();                                     // compute units of the device
 hipError_t launch_kv_convert(uint16_t* cache, uint16_t* nat, int L, int B, int H, int hd, int n,
                              size_t layer_stride, size_t row_stride, size_t kv_stride,
                              size_t head_stride, int to_cache, hipStream_t s);
 
-// Packed bf16 cache: element offsets inside one head region (see attention.hip).
-__host__ __device__ inline size_t kv_k_offset(int p, int i, int hd) {
-  return ((size_t)(p >> 4) * (hd >> 5) + (i >> 5)) * 512 + (((i & 31) >> 3) * 16 + (p & 15)) * 8 +
-         (i & 7);
-}
-__host__ __device__ inline size_t kv_v_offset(int p, int i, int hd) {
-  const int pk = p & 31;
-  const int g = (pk & 15) >> 2, e = (pk & 3) + ((pk >> 4) << 2);
-  return ((size_t)(p >> 5) * (hd >> 4) + (i >> 4)) * 512 + (g * 16 + (i & 15)) * 8 + e;
-}
-// positions a bf16 head region holds (max_len rounded up to whole 32-key blocks)
-inline int kv_capacity(int max_len) { return (max_len + 31) / 32 * 32; }
 
 // forward pieces
 hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,
