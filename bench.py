@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--K", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="K x batch sweep on the 7B shape (one JSON line per point, then a "
+                         "summary line); --steps timed rounds per point")
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
+    ap.add_argument("--sweep-K", default="1,2,3,4,5,6,7,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--verify-only", action="store_true",
@@ -335,6 +340,106 @@ def ar_ms_per_token(binding, torch, model, kv, ws, B, V, knobs, seed, tok0, n_re
     return float(np.median([a.elapsed_time(b) for a, b in ev])) / AR_STEPS
 
 
+def speedup_formula(alpha, K, c):
+    """Expected wall-time improvement ([LENS] "How much faster in practice?")."""
+    e = (1 - alpha ** (K + 1)) / (1 - alpha) if alpha < 1 else K + 1
+    return e / (K * c + 1)
+
+
+def sweep(args):
+    """Where speculation stops paying and which K is best, per batch size: the 7B-shape
+    models built once, one prefilled context per batch size, and for every K a fresh
+    round driver on the same caches rolled back to the context.  Each point: graph-
+    replayed rounds timed as in the main bench, alpha, plain decoding at that batch size,
+    and the tokens/s the measured round time would give at the pages' alpha = 0.8."""
+    import torch
+
+    from speculative_decoding_forward_amd import binding, rounds, synth
+
+    wl = synth.WORKLOADS["7b"]
+    knobs = (wl.temperature, wl.top_k, wl.top_p)
+    V = wl.target.vocab
+    Bs = [int(x) for x in args.sweep_batches.split(",")]
+    Ks = [int(x) for x in args.sweep_K.split(",")]
+    Wt = synth.make_weights(wl.target, seed=args.seed, model_id=synth.TARGET, device="cuda")
+    Wd = synth.make_weights(wl.draft, seed=args.seed, model_id=synth.DRAFT, device="cuda")
+    tm, dm = binding.Model(wl.target, Wt), binding.Model(wl.draft, Wd)
+    del Wt, Wd
+    torch.cuda.empty_cache()
+    warm, steps = 2, args.steps
+    summary = []
+    for B in Bs:
+        max_len = wl.ctx + (warm + steps + 3) * (max(Ks) + 1) + AR_STEPS
+        caches = (binding.KVCache(wl.target, B, max_len), binding.KVCache(wl.draft, B, max_len))
+        ctx = synth.context_ids(args.seed, B, wl.ctx, V)
+        base = rounds.SpecDecoder(wl.target, None, wl.draft, None, B, 1, max_len, knobs,
+                                  seed=args.seed, models=(tm, dm), caches=caches)
+        base.prefill(ctx)
+        torch.cuda.synchronize()
+        lt0, ld0 = caches[0].len.clone(), caches[1].len.clone()
+        tok0 = base.pending.clone()
+        t_ar = ar_ms_per_token(binding, torch, tm, caches[0], base.ws_t, B, V, knobs, args.seed,
+                               tok0, 6)
+        d_ar = ar_ms_per_token(binding, torch, dm, caches[1], base.ws_d, B, V, knobs, args.seed,
+                               tok0, 6)
+        ar_tps = B / (t_ar / 1e3)
+        pts = []
+        for K in Ks:
+            caches[0].len.copy_(lt0)
+            caches[1].len.copy_(ld0)
+            dec = rounds.SpecDecoder(wl.target, None, wl.draft, None, B, K, max_len, knobs,
+                                     seed=args.seed, models=(tm, dm), caches=caches)
+            dec.pending.copy_(tok0)
+            dec.n_pending.fill_(1)
+            for r in range(warm):
+                dec.step(r)
+            dec.set_round(warm)
+            dec.capture()
+            n_hist = torch.zeros((steps, B), dtype=torch.int32, device="cuda")
+            dec.replay()
+            n_hist[0] += dec.n_out
+            n_hist.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                dec.replay()
+                n_hist[i] += dec.n_out
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            hist = n_hist.cpu().numpy().astype(np.int64)
+            assert hist.min() >= 1
+            acc = hist - 1
+            alpha = acc.sum() / max(1, acc.sum() + (acc < K).sum())
+            round_s = wall / steps
+            e08 = (1 - 0.8 ** (K + 1)) / (1 - 0.8)
+            pt = {"sweep_point": True, "batch": B, "K": K, "tokens_per_s": hist.sum() / wall,
+                  "ms_per_round": round_s * 1e3, "tokens_per_round_per_row": hist.mean(),
+                  "alpha_measured": float(alpha), "autoregressive_tokens_per_s": ar_tps,
+                  "c_measured": d_ar / t_ar,
+                  "speedup_measured": hist.sum() / wall / ar_tps,
+                  "speedup_formula": speedup_formula(float(alpha), K, d_ar / t_ar),
+                  "projected_at_alpha_0.8_tokens_per_s": B * e08 / round_s,
+                  "projected_speedup_at_alpha_0.8": B * e08 / round_s / ar_tps}
+            print(json.dumps(pt), flush=True)
+            pts.append(pt)
+            del dec
+        c = d_ar / t_ar
+        best_formula_K = max(range(1, 17), key=lambda k: speedup_formula(0.8, k, c))
+        best = max(pts, key=lambda q: q["projected_at_alpha_0.8_tokens_per_s"])
+        summary.append({"batch": B, "autoregressive_tokens_per_s": ar_tps, "c_measured": c,
+                        "best_K_at_alpha_0.8": best["K"],
+                        "best_projected_speedup_at_alpha_0.8":
+                            best["projected_speedup_at_alpha_0.8"],
+                        "formula_best_K_at_alpha_0.8_and_measured_c": best_formula_K,
+                        "pays_at_alpha_0.8": best["projected_speedup_at_alpha_0.8"] > 1.0,
+                        "best_measured_K": max(pts, key=lambda q: q["tokens_per_s"])["K"],
+                        "best_measured_speedup": max(q["speedup_measured"] for q in pts)})
+        del base, caches
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep_summary": summary, "workload": "7b-shape, context 2048, T=0.8, "
+                      "top-p 0.95, random-init models"}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -358,6 +463,9 @@ def main():
         return
     if args.workload == "accept":
         accept_only(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
     wl = synth.WORKLOADS[args.workload]
     if args.verify_only:

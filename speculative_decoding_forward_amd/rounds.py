@@ -22,17 +22,29 @@ PREFILL_CHUNK = 64
 
 class SpecDecoder:
     def __init__(self, tshape, tweights, dshape, dweights, batch, K, max_len, knobs, seed=0,
-                 device="cuda", prefill_chunk=PREFILL_CHUNK):
+                 device="cuda", prefill_chunk=PREFILL_CHUNK, models=None, caches=None):
+        """models = (target, draft) binding.Model and caches = (target, draft)
+        binding.KVCache already built (the weights arguments are then unused): several
+        decoders -- e.g. one per K -- can share one copy of the models and one prefilled
+        context."""
         if tshape.vocab != dshape.vocab:
             raise ValueError("draft and target must share the vocabulary")
         self.B, self.K, self.max_len = batch, K, max_len
         self.knobs, self.seed, self.device = tuple(knobs), int(seed), device
         self.chunk = prefill_chunk
         V = tshape.vocab
-        self.target = binding.Model(tshape, tweights)
-        self.draft = binding.Model(dshape, dweights)
-        self.tkv = binding.KVCache(tshape, batch, max_len, device)
-        self.dkv = binding.KVCache(dshape, batch, max_len, device)
+        if models is not None:
+            self.target, self.draft = models
+        else:
+            self.target = binding.Model(tshape, tweights)
+            self.draft = binding.Model(dshape, dweights)
+        if caches is not None:
+            self.tkv, self.dkv = caches
+            if self.tkv.max_len < max_len or self.dkv.max_len < max_len:
+                raise ValueError("shared caches are shorter than max_len")
+        else:
+            self.tkv = binding.KVCache(tshape, batch, max_len, device)
+            self.dkv = binding.KVCache(dshape, batch, max_len, device)
         rows = max(K + 1, prefill_chunk)
         self.ws_t = self.target.workspace(batch, rows, max_len, device)
         self.ws_d = self.draft.workspace(batch, rows, max_len, device)
