@@ -130,9 +130,10 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.tok_eff = (int32_t*)take(R * 4);
   w.tok2 = (int32_t*)take((size_t)B * 2 * 4);
   w.ntok2 = (int32_t*)take(B * 4);
-  // attention completion counters [B*H*ceil(M/8)] followed by 64 zero words; prep
-  // clears all of them at the start of every forward
-  w.n_counters = B * c.n_heads * attn_groups(M) + 64;
+  // attention completion counters (one per (row, head, query group), kAttnCounterStride
+  // words apart) followed by 64 zero words; prep clears all of them at the start of
+  // every forward
+  w.n_counters = B * c.n_heads * attn_groups(M) * kAttnCounterStride + 64;
   w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
   w.h = take(R * d * e);

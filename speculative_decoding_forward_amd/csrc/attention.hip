@@ -285,7 +285,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
                                             kCoherentSc1);
   }
   // count this workgroup in once its partial is written
-  const int cidx = (b * H + h) * NG + qg;
+  const int cidx = ((b * H + h) * NG + qg) * kAttnCounterStride;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
@@ -342,11 +342,16 @@ int attn_max_splits(int B, int H, int M, int max_len) {
 
 // Splits per (row, head, query group): as many as make the grid one workgroup per
 // compute unit (a CU holding two workgroups streams its two shares at half the rate
-// and finishes last), and at most one per block.  A split takes `bps` consecutive
-// blocks (attn_bps), the workgroup's waves round-robin.
+// and finishes last), but no more than leave every wave of a workgroup at least one
+// block (kAttnMinBlocksPerSplit): more, smaller splits only lengthen the merge -- at
+// one or two queries per row (the draft's steps) 14 splits of 5 blocks took 11.4 us
+// where 7 of 10 took 10.8.  A split takes `bps` consecutive blocks (attn_bps), the
+// workgroup's waves round-robin.
+constexpr int kAttnMinBlocksPerSplit = SPEC_ATTN_WAVES;
 int attn_nsplit(int B, int H, int M, int max_len) {
   const int blocks = cdiv(max_len, AKB), groups = B * H * cdiv(M, AQ);
   int ns = std::max(1, std::min(device_cus(), kAttnMaxCUs) / groups);
+  ns = std::min(ns, std::max(1, blocks / kAttnMinBlocksPerSplit));
   ns = std::min(ns, attn_max_splits(B, H, M, max_len));
   // the same split count with fewer blocks per split would leave splits empty: shrink
   // it to the number that the per-split block count really needs

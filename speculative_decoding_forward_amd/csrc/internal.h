@@ -61,6 +61,9 @@ hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const ui
                                  float* part, unsigned* counters, int max_len, uint16_t* out,
                                  hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 constexpr int kAttnMaxCUs = 1024;                     // bound on the CUs a split grid uses
+// completion counters of the split attention sit 128 bytes apart: the atomics of
+// different (row, head, group) units then do not queue on one cache line
+constexpr int kAttnCounterStride = 32;
 int attn_nsplit(int B, int H, int M, int max_len);  // splits per (row, head, group)
 int attn_max_splits(int B, int H, int M, int max_len);  // bound of attn_nsplit (workspace)
 int attn_groups(int M);                               // query groups per row
