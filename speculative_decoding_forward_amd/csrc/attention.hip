@@ -342,16 +342,16 @@ int attn_max_splits(int B, int H, int M, int max_len) {
 
 // Splits per (row, head, query group): as many as make the grid one workgroup per
 // compute unit (a CU holding two workgroups streams its two shares at half the rate
-// and finishes last), but no more than leave every wave of a workgroup at least one
-// block (kAttnMinBlocksPerSplit): more, smaller splits only lengthen the merge -- at
-// one or two queries per row (the draft's steps) 14 splits of 5 blocks took 11.4 us
-// where 7 of 10 took 10.8.  A split takes `bps` consecutive blocks (attn_bps), the
-// workgroup's waves round-robin.
-constexpr int kAttnMinBlocksPerSplit = SPEC_ATTN_WAVES;
+// and finishes last), but no more than give each split about 1.5 blocks per wave
+// (kAttnBlocksPerSplit): more, smaller splits only lengthen the merge.  Over a 69-block
+// capacity, 8 or 14 splits (9 or 5 blocks) took 14.2 / 11.1 us at 6 / 1 queries per
+// row, 6 splits of 12 blocks 13.6 / 10.6 us, 5 of 16 and 3 of 24 longer again.  A split
+// takes `bps` consecutive blocks (attn_bps), the workgroup's waves round-robin.
+constexpr int kAttnBlocksPerSplit = 3 * SPEC_ATTN_WAVES / 2;
 int attn_nsplit(int B, int H, int M, int max_len) {
   const int blocks = cdiv(max_len, AKB), groups = B * H * cdiv(M, AQ);
   int ns = std::max(1, std::min(device_cus(), kAttnMaxCUs) / groups);
-  ns = std::min(ns, std::max(1, blocks / kAttnMinBlocksPerSplit));
+  ns = std::min(ns, cdiv(blocks, kAttnBlocksPerSplit));
   ns = std::min(ns, attn_max_splits(B, H, M, max_len));
   // the same split count with fewer blocks per split would leave splits empty: shrink
   // it to the number that the per-split block count really needs
