@@ -162,26 +162,51 @@ def test_rollback():
     assert np.array_equal(kv.len.cpu().numpy(), [4, 10])
 
 
+def _matmul_f32_ksteps(a, w, step=128):
+    """a @ w.T accumulated in float32 over consecutive 128-wide K steps (the structure
+    of an fp32-accumulating K loop)."""
+    a32, w32 = np.asarray(a, np.float32), np.asarray(w, np.float32)
+    acc = None
+    for k0 in range(0, a32.shape[-1], step):
+        part = a32[..., k0:k0 + step] @ w32[:, k0:k0 + step].T
+        acc = part if acc is None else (acc + part).astype(np.float32)
+    return acc.astype(np.float64)
+
+
 def oracle_spread(fn):
-    """Run an oracle computation as written and in two other evaluations that are just
+    """Run an oracle computation as written and in four other evaluations that are just
     as correct for a bf16 model with fp32 accumulation: every bf16 rounding taken from
-    the float32-rounded value, and every matrix product accumulated in float32.  The
-    largest elementwise difference from the first run is the spread that rounding and
-    accumulation order alone produce (bf16 rounding flips cascade through the layers)."""
+    the float32-rounded value; every value perturbed by a seeded relative 2^-18 before
+    its bf16 rounding (the size of fp32 accumulation error over a few thousand terms,
+    sqrt(K) * 2^-24); every matrix product accumulated in float32; and every product
+    accumulated in float32 over 128-wide K steps.  The largest elementwise difference
+    from the first run is the spread that rounding and accumulation order alone produce:
+    a value that lands on the other side of a bf16 rounding boundary moves by one bf16
+    step, and such moves cascade through the layers."""
     o1 = fn()
     orig_rb, orig_mm = omodel.round_bf16, omodel.matmul
     try:
         omodel.round_bf16 = lambda x: orig_rb(np.asarray(x, np.float64).astype(np.float32))
         o2 = fn()
+        rng = np.random.default_rng(12345)
+
+        def rb_perturbed(x):
+            x = np.asarray(x, np.float64)
+            return orig_rb(x * (1.0 + 2.0 ** -18 * rng.uniform(-1.0, 1.0, x.shape)))
+
+        omodel.round_bf16 = rb_perturbed
+        o5 = fn()
     finally:
         omodel.round_bf16 = orig_rb
     try:
         omodel.matmul = lambda a, w: (np.asarray(a, np.float32) @
                                       np.asarray(w, np.float32).T).astype(np.float64)
         o3 = fn()
+        omodel.matmul = _matmul_f32_ksteps
+        o4 = fn()
     finally:
         omodel.matmul = orig_mm
-    return o1, np.maximum(np.abs(o2 - o1), np.abs(o3 - o1))
+    return o1, np.max(np.stack([np.abs(o - o1) for o in (o2, o3, o4, o5)]), axis=0)
 
 
 def assert_bf16_logits(g, o, spread, what):
@@ -240,6 +265,53 @@ def test_full_depth_small():
     g, o, spread, st = synthetic_kv_case("small", 1, 4)
     assert np.all(st == 0)
     assert_bf16_logits(g, o, spread, "small 24 layers")
+
+
+@pytest.mark.parametrize("B,n_in", [(1, 2), (1, 1), (2, 1)])
+def test_draft_steps_match_oracle(B, n_in):
+    """Draft steps through the C ABI at the 7B draft's full width (2 layers, context 2048):
+    the draft logits of step 0 (n_in pending tokens at two rows; one pending token leaves
+    a padding row) and step 1 against the oracle's forward of the same tokens, and bitwise
+    equal to the verify entry point's logits for the same tokens and cache."""
+    wl = synth.WORKLOADS["7b"]
+    shape = dataclasses.replace(wl.draft, n_layers=2)
+    m, Wn = setup(shape, seed=3, model_id=synth.DRAFT)
+    K, V = 2, shape.vocab
+    max_len = wl.ctx + 4
+    kv = binding.KVCache(shape, B, max_len)
+    fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=3, device=DEV)
+    kv.import_(fill)
+    kv.len.fill_(wl.ctx)
+    toks = synth.context_ids(11, B, 2, V)
+    in_np = np.full((B, 2), -1, np.int32)
+    in_np[:, :n_in] = toks[:, :n_in]
+    in_tok, n_in_t = to_dev(in_np), to_dev(np.full(B, n_in, np.int32))
+    x_tilde = torch.zeros((B, K), dtype=torch.int32, device=DEV)
+    q_logits = torch.zeros((B, K, V), dtype=torch.float32, device=DEV)
+    ws = m.workspace(B, 2, max_len)
+    for step in range(K):
+        binding.draft_step(m, kv, in_tok, n_in_t, step, (0.8, 0, 0.95), 7, 0, x_tilde,
+                           q_logits, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(kv.len.cpu().numpy(), [wl.ctx + n_in + 1] * B)
+    seq = np.concatenate([toks[:, :n_in], x_tilde.cpu().numpy()[:, :1]], axis=1)
+    fill_np = fill.float().cpu().numpy()
+
+    def run():
+        oc = omodel.KVCache(shape, B, max_len)
+        oc.fill(fill_np, [wl.ctx] * B)
+        return omodel.forward(shape, Wn, oc, seq)
+
+    o, spread = oracle_spread(run)
+    g = q_logits.cpu().numpy()
+    # the same tokens through the verify entry point (the attention kernel's own merge)
+    kv2 = binding.KVCache(shape, B, max_len)
+    kv2.import_(fill)
+    kv2.len.fill_(wl.ctx)
+    gv, _ = gpu_forward(m, kv2, seq)
+    assert np.array_equal(g[:, 0], gv[:, n_in - 1]) and np.array_equal(g[:, 1], gv[:, n_in])
+    assert_bf16_logits(g[:, 0], o[:, n_in - 1], spread[:, n_in - 1], f"draft step 0 B={B} n_in={n_in}")
+    assert_bf16_logits(g[:, 1], o[:, n_in], spread[:, n_in], f"draft step 1 B={B} n_in={n_in}")
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, None), ("7b", 1, None), ("7b", 8, None),
