@@ -430,7 +430,10 @@ __device__ __forceinline__ void load_row(float (&v)[VPT], const float* row, int 
 
 // One workgroup per (b, j), j = 0..K.  Writes res_acc[b*K + j] (j < K), res_cand[b*(K+1)+j]
 // and res_status[b*(K+1)+j].  While the draft row is processed, the processed target
-// row waits in the LDS weight buffer (one row in registers at a time).
+// row waits in the LDS weight buffer (one row in registers at a time).  Workgroups
+// 0 .. B*K-1 take the positions with a draft row (b = id / K, j = id % K) and the last B
+// the bonus rows (j = K): with more workgroups than compute units, those that start
+// late are then the bonus rows, which process one row instead of two.
 template <int VPT>
 __global__ __launch_bounds__(VT) void k_accept_rows(
     const float* __restrict__ p_logits, const float* __restrict__ q_logits,
@@ -440,7 +443,8 @@ __global__ __launch_bounds__(VT) void k_accept_rows(
     float* __restrict__ dbg_q) {
   __shared__ VocabLDS sh;
   if (round_dev) round = *round_dev;
-  const int b = blockIdx.x / (K + 1), j = blockIdx.x % (K + 1), tid = threadIdx.x;
+  const int nbk = (int)(gridDim.x / (K + 1)) * K, id = blockIdx.x;
+  const int b = id < nbk ? id / K : id - nbk, j = id < nbk ? id % K : K, tid = threadIdx.x;
   const bool has_q = j < K;
   const float* prow = p_logits + ((size_t)b * (K + 1) + j) * V;
   int status = 0;
