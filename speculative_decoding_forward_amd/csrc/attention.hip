@@ -15,13 +15,15 @@
 // Every wave load is therefore 1 KB contiguous.
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
-// (b, h) and one group of up to 16 queries; the split count makes the grid one
-// workgroup per compute unit.  Its waves (8 for head_dim 128) take the blocks
+// (b, h) and one group of up to 16 queries; the split count makes the grid at most one
+// workgroup per compute unit and leaves each split about 1.5 blocks per wave
+// (attn_nsplit).  Its waves (8 for head_dim 128) take the blocks
 // round-robin, keep two blocks of K and V in flight each -- with a split's blocks thus
 // all requested at once -- and run an online softmax per query.  The
 // wave states merge in LDS; with more than one split the workgroup partial goes to
-// global memory and the last workgroup of (b, h, qg) to finish merges them in split
-// order and writes the bf16 output.  P enters the second product as bf16 hi + lo
+// global memory and the last workgroup of (b, h, qg) to finish -- found by a
+// completion counter, one per (b, h, qg), 128 bytes apart -- merges them in split order
+// and writes the bf16 output.  P enters the second product as bf16 hi + lo
 // parts (two MFMAs), which keeps its value to ~16 bits.
 #include <hip/hip_ext.h>
 #include <math.h>
