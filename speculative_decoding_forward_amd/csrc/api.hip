@@ -93,7 +93,6 @@ struct FwdWS {
   int32_t* pos0;
   int32_t* ntok_eff;
   int32_t* tok_eff;
-  int32_t* tok2;      // draft-step input tokens [B, 2]
   int32_t* ntok2;     // draft-step counts [B]
   unsigned* counters; // completion counters: [B*H] attention + 1 GEMM
   int n_counters;
@@ -128,7 +127,6 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.pos0 = (int32_t*)take(B * 4);
   w.ntok_eff = (int32_t*)take(B * 4);
   w.tok_eff = (int32_t*)take(R * 4);
-  w.tok2 = (int32_t*)take((size_t)B * 2 * 4);
   w.ntok2 = (int32_t*)take(B * 4);
   // attention completion counters (one per (row, head, query group), kAttnCounterStride
   // words apart) followed by 64 zero words; prep clears all of them at the start of
@@ -356,10 +354,11 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
 // The forward pass shared by the verify call, draft steps and prefill chunks.
 spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
                     const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
-                    int record_base, const FwdWS& w, hipStream_t s) {
+                    int record_base, const FwdWS& w, hipStream_t s,
+                    const DraftSrc* ds = nullptr) {
   SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, m->cfg.vocab, kv->len, kv->base, record_base,
                           kv->max_len, w.pos0, w.ntok_eff, w.tok_eff, row_status, w.counters,
-                          w.n_counters, s));
+                          w.n_counters, ds, s));
   if (m->cfg.dtype == SPEC_DT_BF16) return forward_bf16(m, kv, B, M, logits, w, s);
   return forward_f32(m, kv, B, M, logits, w, s);
 }
@@ -700,9 +699,9 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
   const FwdWS w = fwd_layout(draft->cfg, B, M, dkv->max_len, (char*)ws);
   if (ws_bytes < w.total) return SPEC_E_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
-  SPEC_LAUNCH(launch_draft_tokens(in_tok, n_in, x_tilde, B, K, step, w.tok2, w.ntok2, s));
-  spec_status st =
-      forward(draft, dkv, w.tok2, w.ntok2, B, M, w.logits, row_status, step == 0 ? 1 : 0, w, s);
+  const DraftSrc ds{in_tok, n_in, x_tilde, K, step, w.ntok2};
+  spec_status st = forward(draft, dkv, nullptr, nullptr, B, M, w.logits, row_status,
+                           step == 0 ? 1 : 0, w, s, &ds);
   if (st != SPEC_OK) return st;
   SPEC_LAUNCH(launch_draft_sample(w.logits, B, M, w.ntok2, step, K, draft->cfg.vocab,
                                   to_knobs(knobs), seed, round, round_dev, x_tilde, q_logits,

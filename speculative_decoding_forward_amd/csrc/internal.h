@@ -73,11 +73,21 @@ hipError_t launch_kv_convert(uint16_t* cache, uint16_t* nat, int L, int B, int H
 
 
 // forward pieces
+// Input tokens of a draft step, assembled by the prep kernel itself: step 0 takes the
+// n_in[b] (1 or 2) pending tokens in_tok[b, 0..1], step s > 0 the draft token
+// x_tilde[b, s - 1]; the per-row count also goes to n_tok_out (the sampler reads it).
+struct DraftSrc {
+  const int32_t* in_tok;
+  const int32_t* n_in;
+  const int32_t* x_tilde;
+  int K, step;
+  int32_t* n_tok_out;
+};
 hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,
                        int32_t* len, int32_t* base, int record_base, int max_len,
                        int32_t* pos0, int32_t* ntok_eff, int32_t* tok_eff,
                        int32_t* row_status, unsigned* counters, int n_counters,
-                       hipStream_t s);
+                       const DraftSrc* ds, hipStream_t s);
 hipError_t launch_embed(const void* embed, int dtype, const int32_t* tok_eff, int R, int d,
                         float* x, hipStream_t s);
 hipError_t launch_norm_input(const float* x, const float* g, int R, int d, float eps,
@@ -110,9 +120,6 @@ hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t*
                                int step, int K, int V, SamplingKnobs kn, uint64_t seed,
                                uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
                                float* q_logits, hipStream_t s);
-hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
-                               const int32_t* x_tilde, int B, int K, int step,
-                               int32_t* tokens, int32_t* n_tok, hipStream_t s);
 hipError_t launch_rollback(int32_t* len, const int32_t* new_len, int B, hipStream_t s);
 hipError_t launch_verify_tokens(const int32_t* pending, const int32_t* n_pending,
                                 const int32_t* x_tilde, int B, int K, int32_t* tokens,

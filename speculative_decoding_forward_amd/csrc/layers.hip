@@ -21,18 +21,26 @@ namespace specdec {
 // ------------------------------------------------------------------ bookkeeping ----
 
 // One thread per row b: effective token count (0 on cache overflow), start position,
-// validated token ids, and the length update.
+// validated token ids, and the length update.  A draft step (draft != 0) takes its
+// tokens from the DraftSrc instead of tokens / n_tok.
 __global__ void k_prep(const int32_t* __restrict__ tokens, const int32_t* __restrict__ n_tok,
                        int B, int M, int V, int32_t* __restrict__ len,
                        int32_t* __restrict__ base, int record_base, int max_len,
                        int32_t* __restrict__ pos0, int32_t* __restrict__ ntok_eff,
                        int32_t* __restrict__ tok_eff, int32_t* __restrict__ row_status,
-                       unsigned* __restrict__ counters, int n_counters) {
+                       unsigned* __restrict__ counters, int n_counters, DraftSrc ds,
+                       int draft) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   // completion counters of the fused kernels start each forward at zero
   for (int i = b; i < n_counters; i += gridDim.x * blockDim.x) counters[i] = 0u;
   if (b >= B) return;
-  int n = n_tok ? n_tok[b] : M;
+  int n;
+  if (draft) {
+    n = ds.step == 0 ? min(max(ds.n_in[b], 0), 2) : 1;
+    ds.n_tok_out[b] = n;
+  } else {
+    n = n_tok ? n_tok[b] : M;
+  }
   n = min(max(n, 0), M);
   const int L = len[b];
   int flags = 0;
@@ -43,7 +51,8 @@ __global__ void k_prep(const int32_t* __restrict__ tokens, const int32_t* __rest
   for (int j = 0; j < M; ++j) {
     int t = 0;
     if (j < n) {
-      t = tokens[(size_t)b * M + j];
+      t = !draft ? tokens[(size_t)b * M + j]
+                 : (ds.step == 0 ? ds.in_tok[2 * b + j] : ds.x_tilde[b * ds.K + ds.step - 1]);
       if (t < 0 || t >= V) {
         flags |= SPEC_ROW_BAD_TOKEN;
         t = 0;
@@ -251,11 +260,13 @@ hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M
                        int32_t* len, int32_t* base, int record_base, int max_len,
                        int32_t* pos0, int32_t* ntok_eff, int32_t* tok_eff,
                        int32_t* row_status, unsigned* counters, int n_counters,
-                       hipStream_t s) {
+                       const DraftSrc* ds, hipStream_t s) {
   const int threads = std::max(B, n_counters);
+  if (ds && (ds->step < 0 || (ds->step == 0 ? M < 2 : M < 1))) return hipErrorInvalidValue;
   k_prep<<<cdiv(threads, 256), 256, 0, s>>>(tokens, n_tok, B, M, V, len, base, record_base,
                                             max_len, pos0, ntok_eff, tok_eff, row_status,
-                                            counters, n_counters);
+                                            counters, n_counters, ds ? *ds : DraftSrc{},
+                                            ds ? 1 : 0);
   return hipGetLastError();
 }
 

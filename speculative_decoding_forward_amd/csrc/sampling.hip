@@ -610,23 +610,6 @@ __global__ __launch_bounds__(VT) void k_draft_sample(
   if (tid == 0) x_tilde[b * K + step] = x;
 }
 
-// Builds the token matrix [B, 2] / counts for a draft step.
-__global__ void k_draft_tokens(const int32_t* __restrict__ in_tok, const int32_t* __restrict__ n_in,
-                               const int32_t* __restrict__ x_tilde, int B, int K, int step,
-                               int32_t* __restrict__ tokens, int32_t* __restrict__ n_tok) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  if (step == 0) {
-    const int n = min(max(n_in[b], 0), 2);
-    tokens[2 * b] = in_tok[2 * b];
-    tokens[2 * b + 1] = n > 1 ? in_tok[2 * b + 1] : 0;
-    n_tok[b] = n;
-  } else {
-    tokens[b] = x_tilde[b * K + step - 1];
-    n_tok[b] = 1;
-  }
-}
-
 // tokens[b] = [pending[b, n_pending[b] - 1], x~_0 .. x~_{K-1}]
 __global__ void k_verify_tokens(const int32_t* __restrict__ pending,
                                 const int32_t* __restrict__ n_pending,
@@ -684,13 +667,6 @@ hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t*
                                float* q_logits, hipStream_t s) {
   VPT_DISPATCH(V, (k_draft_sample<P><<<B, VT, 0, s>>>(logits, M, n_in, step, K, V, kn, seed,
                                                      round, round_dev, x_tilde, q_logits)));
-  return hipGetLastError();
-}
-
-hipError_t launch_draft_tokens(const int32_t* in_tok, const int32_t* n_in,
-                               const int32_t* x_tilde, int B, int K, int step,
-                               int32_t* tokens, int32_t* n_tok, hipStream_t s) {
-  k_draft_tokens<<<cdiv(B, 64), 64, 0, s>>>(in_tok, n_in, x_tilde, B, K, step, tokens, n_tok);
   return hipGetLastError();
 }
 
