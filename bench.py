@@ -34,7 +34,8 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_verify_7b_b1_k5_traffic.m
 GEMM_SOURCES = ["speculative_decoding_forward_amd/csrc/gemm.hip",
                 "speculative_decoding_forward_amd/csrc/common.h",
                 "speculative_decoding_forward_amd/csrc/gemm.h",
-                "speculative_decoding_forward_amd/csrc/kv_layout.h"]
+                "speculative_decoding_forward_amd/csrc/kv_layout.h",
+                "speculative_decoding_forward_amd/csrc/act_layout.h"]
 
 
 def parse():

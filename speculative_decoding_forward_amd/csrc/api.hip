@@ -134,11 +134,12 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.n_counters = B * c.n_heads * attn_groups(M) * kAttnCounterStride + 64;
   w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
-  w.h = take(R * d * e);
-  w.a = take(R * F * e);
+  // the GEMMs' bf16 inputs in the packed activation order (whole 16-row tiles)
+  w.h = take((size_t)act_rows(R) * d * e);
+  w.a = take((size_t)act_rows(R) * F * e);
   w.y = (float*)take(c.dtype == SPEC_DT_F32 ? R * std::max(3 * d, ffn_out) * 4 : 0);
   w.q = take(R * d * e);
-  w.att = take(R * d * e);
+  w.att = take((size_t)act_rows(R) * d * e);
   w.part = (float*)take(c.dtype == SPEC_DT_BF16
                             ? (size_t)B * c.n_heads * nsplit * M * (c.head_dim + 2) * 4
                             : 0);

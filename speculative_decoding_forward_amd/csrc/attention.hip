@@ -30,6 +30,7 @@
 
 #include <algorithm>
 
+#include "act_layout.h"
 #include "common.h"
 #include "internal.h"
 
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     // no query of this row in this group: the first split writes the padding rows
     if (split == 0)
       for (int idx = threadIdx.x; idx < (jend - qg * AQ) * HD; idx += AW * 64)
-        out[((size_t)b * M + qg * AQ + idx / HD) * d + h * HD + idx % HD] = 0;
+        out[act_index(b * M + qg * AQ + idx / HD, h * HD + idx % HD, d)] = 0;
     return;
   }
   if (split >= n_active) return;  // uniform over the workgroup
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
         ov[k] = j < nq ? (f32_to_bf16(v[2 * k] / lsum) |
                           ((uint32_t)f32_to_bf16(v[2 * k + 1] / lsum) << 16))
                        : 0u;
-      u16* dst = out + ((size_t)b * M + j) * d + h * HD + tt * DPT;
+      u16* dst = out + act_index(b * M + j, h * HD + tt * DPT, d);  // DPT columns contiguous
       if constexpr (DPT == 8)
         *reinterpret_cast<uint4*>(dst) = uint4{ov[0], ov[1], ov[2], ov[3]};
       else
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     }
     const uint32_t lo = f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
     const uint32_t hi = f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-    *reinterpret_cast<uint2*>(out + ((size_t)b * M + jr) * d + h * HD + c4) = uint2{lo, hi};
+    *reinterpret_cast<uint2*>(out + act_index(b * M + jr, h * HD + c4, d)) = uint2{lo, hi};
   }
   if (threadIdx.x == 0) counters[cidx] = 0u;
 }

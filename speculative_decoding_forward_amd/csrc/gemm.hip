@@ -41,6 +41,7 @@
 #include <algorithm>
 #include <math.h>
 
+#include "act_layout.h"
 #include "common.h"
 #include "gemm.h"
 #include "kv_layout.h"
@@ -303,7 +304,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
           const float xo = L.xres[rr * 16 + nl];
           xn = xo + v[e];
           g.x[(size_t)r * g.N + col] = xn;
-          g.h_out[(size_t)r * g.N + col] = f32_to_bf16(xn * gc);
+          g.h_out[act_index(r, col, g.N)] = f32_to_bf16(xn * gc);
         }
         sq[e] = (double)xn * xn;
       }
@@ -368,14 +369,14 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
         const float y = v[e];
         const float yp = __shfl_xor(y, 8);  // the up column paired with gate column nl
         if (r < R && !is_hi)
-          g.act_out[(size_t)r * g.N1 + 8 * t + nl] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
+          g.act_out[act_index(r, 8 * t + nl, g.N1)] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
       }
     } else if (mode == EPI_GELU) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r0 + mt * 16 + 4 * gq + e;
         if (r < R)
-          g.act_out[(size_t)r * g.N + 16 * t + nl] =
+          g.act_out[act_index(r, 16 * t + nl, g.N)] =
               f32_to_bf16(0.5f * v[e] * (1.f + erff(v[e] * 0.70710678118654752f)));
       }
     } else {  // EPI_STORE
@@ -537,7 +538,9 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   for (int mt = 0; mt < MT; ++mt) {
     const int r = r0 + mt * 16 + nl;
     aok[mt] = r < R;
-    arow[mt] = g.A + (size_t)(aok[mt] ? r : 0) * g.lda + 8 * gq;
+    // packed activations (act_layout.h): this lane's 16 bytes of step js, slice s sit at
+    // arow[mt] + js * 2048 + s * 512
+    arow[mt] = g.A + (size_t)(blockIdx.y * MT + mt) * (size_t)nsuper * 2048 + 8 * (4 * nl + gq);
   }
   floatx4 acc[MT][NT];
 #pragma unroll
@@ -557,7 +560,6 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   auto issue = [&](int slot) {
     const bool valid = is <= last_step && wact && it < nt;
     const int js = wact ? wv + (is <= last_step ? is : last_step) * GW : 0;  // super-step
-    const int kb = js * 128;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -567,7 +569,8 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        af[slot][mt][s] = ld8((valid && aok[mt]) ? arow[mt] + kb + 32 * s : zblk, true);
+        af[slot][mt][s] = ld8((valid && aok[mt]) ? arow[mt] + (size_t)js * 2048 + 512 * s : zblk,
+                              true);
     if (++is == S) {
       is = 0;
       ++it;
@@ -744,14 +747,19 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
       const int wvu = __builtin_amdgcn_readfirstlane(wv);
       const bool wactu = wvu < nsuper;
       const int lastu = wactu ? (nsuper - 1 - wvu) / GW : 0;
-      const uint32_t a_bytes = (uint32_t)g.R * (uint32_t)g.lda * 2u;
+      // packed activations (act_layout.h): row tile mt_abs, step js, slice s of this lane
+      // at byte mt_abs * nsuper * 4096 + js * 4096 + s * 1024 + 16 * (4 * nl + gq); the
+      // direct-to-LDS load still lands lane l's 16 bytes at 16 * l of the slot
+      const uint32_t a_bytes = (uint32_t)act_rows(g.R) * (uint32_t)g.K * 2u;
       const __amdgpu_buffer_rsrc_t ra = coherent_rsrc(g.A, a_bytes);
       const __amdgpu_buffer_rsrc_t rw = coherent_rsrc(g.W, (size_t)g.ntiles * tile_elems * 2);
       uint32_t aoff[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = r0 + mt * 16 + nl;
-        aoff[mt] = r < g.R ? ((uint32_t)r * (uint32_t)g.lda + 8u * gq) * 2u : a_bytes;
+        aoff[mt] = r < g.R ? ((uint32_t)(r0 / 16 + mt) * (uint32_t)nsuper * 4096u +
+                              16u * (uint32_t)(4 * nl + gq))
+                           : a_bytes;
       }
       const uint32_t woff = 16u * lane;
       uint32_t wtile[TPW];  // byte offset of each tile of the chunk (uniform)
@@ -759,12 +767,12 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
       for (int j = 0; j < TPW; ++j) wtile[j] = (uint32_t)tile_of(c, j) * (uint32_t)tile_elems * 2u;
       char* aslot = reinterpret_cast<char*>(&part[0][0][0][0]) + (size_t)wvu * MT * 4 * 1024;
       auto dmaA = [&](int i) {
-        const uint32_t so = (wactu && i <= lastu) ? (uint32_t)(wvu + i * GW) * 256u : a_bytes;
+        const uint32_t so = (wactu && i <= lastu) ? (uint32_t)(wvu + i * GW) * 4096u : a_bytes;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            buffer_to_lds16(ra, aslot + (mt * 4 + s) * 1024, aoff[mt] + 64u * s, so);
+            buffer_to_lds16(ra, aslot + (mt * 4 + s) * 1024, aoff[mt] + 1024u * s, so);
       };
       auto readA = [&]() {
 #pragma unroll

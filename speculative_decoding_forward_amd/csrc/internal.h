@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/specdec.h"
+#include "act_layout.h"
 #include "gemm.h"
 #include "kv_layout.h"
 

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 
+#include "act_layout.h"
 #include "common.h"
 #include "internal.h"
 
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(
   const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)tok[r] * d);
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
   const float4* gr = reinterpret_cast<const float4*>(g);
-  uint4* hr = reinterpret_cast<uint4*>(h + (size_t)r * d);
+  // h in the packed activation order (act_layout.h): 8 consecutive columns stay contiguous
   const int np = d / 16;
   for (int c = threadIdx.x; c < np; c += 256) {
     double sq = 0.0;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(
       for (int k = 0; k < 4; ++k)
         o[k] = f32_to_bf16(v[2 * k] * gg[2 * k]) |
                ((uint32_t)f32_to_bf16(v[2 * k + 1] * gg[2 * k + 1]) << 16);
-      hr[c8] = uint4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<uint4*>(h + act_index(r, 8 * c8, d)) = uint4{o[0], o[1], o[2], o[3]};
 #pragma unroll
       for (int k = 0; k < 8; ++k) sq += (double)v[k] * v[k];
     }
