@@ -249,12 +249,15 @@ def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
                                          ("small", 8, 7), ("7b", 8, 7), ("7b", 8, 3),
-                                         ("7b", 5, 6), ("70b", 1, 4)])
+                                         ("7b", 5, 6), ("70b", 1, 4), ("7b", 16, 4),
+                                         ("small", 12, 7)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
     layers of the target.  Rows 6 and 5 take the one-row-tile GEMM; 32, 35 (a ragged last
     row tile), 48 and 64 rows the K-outer GEMM with two to four row tiles where a
-    workgroup owns several column tiles, else the tile-at-a-time one."""
+    workgroup owns several column tiles, else the tile-at-a-time one; 80 and 96 rows
+    split into row blocks of at most 64 (64 + 16 and 64 + 32), each on its share of
+    the grid."""
     g, o, spread, st = synthetic_kv_case(wl_name, B, K, layers=2)
     assert np.all(st == 0)
     assert_bf16_logits(g, o, spread, f"{wl_name} B={B} K={K} 2 layers")
