@@ -17,23 +17,24 @@ in tests/test_oracle_model.py.
 Layer spec (pre-norm decoder, no biases, untied embedding and LM head):
   x = E[tok]                                     residual stream (float64 here)
   per layer:
-    q, k, v = N(x, g1) W_qkv^T                   W_qkv rows: [q heads | k heads | v heads]
+    h = bf16(RMSNorm(x) * g1)
+    q, k, v = h W_qkv^T                          W_qkv rows: [q heads | k heads | v heads]
     RoPE on q, k at absolute position (half-split pairs (i, i + hd/2),
        angle = pos * theta^(-2i/hd))
     q, k, v = bf16(.); k, v appended to the cache
     o = bf16(softmax(q K^T / sqrt(hd), causal) V)
-    x += o W_o^T
-    GELU:   a = bf16(gelu(N(x, g2) W1^T)),                  x += a W2^T
-    SwiGLU: a = bf16(silu(N(x, g2) Wg^T) * (N(x, g2) Wu^T)), x += a Wd^T
-  logits = N(x, g_f) W_head^T
-with the RMS-normalised product
-    N(x, g) W^T = s(x) * (bf16(x * g) W^T),   s(x) = 1 / sqrt(mean(x^2) + eps)
-per row: RMSNorm(x) * g = s(x) * (x * g), and the row factor s(x) is taken out of the
-product, so the matrix input is rounded to bf16 before normalisation and the fp32
-product row is scaled after it (the same quantity as bf16(RMSNorm(x) * g) W^T up to
-where the one bf16 rounding falls).  gelu(t) = t * Phi(t), silu(t) = t / (1 + e^-t).
-For float32 models every bf16() is the identity.  Arithmetic is float64 throughout;
-bf16() rounds the float64 value to nearest-even bf16 directly.
+    x += o W_o^T                                 (the "attention half" of the layer)
+    h = bf16(RMSNorm(x) * g2)
+    GELU:   a = bf16(gelu(h W1^T)),              x += a W2^T
+    SwiGLU: a = bf16(silu(h Wg^T) * (h Wu^T)),   x += a Wd^T   (the "FFN half")
+  logits = bf16(RMSNorm(x) * g_f) W_head^T
+with RMSNorm(x) = x / sqrt(mean(x^2) + eps) per row, gelu(t) = t * Phi(t),
+silu(t) = t / (1 + e^-t).  For float32 models every bf16() is the identity.  Arithmetic
+is float64 throughout; bf16() rounds the float64 value to nearest-even bf16 directly.
+
+The halves are exposed on their own (attention_half, ffn_half, lm_head) so a test can
+feed one of them the residual rows another implementation produced and compare that
+half alone.
 
 Weights are given as float32 numpy arrays (bf16-representable values for bf16 models)
 in a dict with keys: embed [V,d], head [V,d], norm_f [d], and per layer l:
@@ -83,19 +84,6 @@ def rmsnorm(x, g, eps):
     x = np.asarray(x, dtype=np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
-
-
-def rms_scale(x, eps):
-    """s(x) = 1 / sqrt(mean(x^2) + eps) per row (float64)."""
-    x = np.asarray(x, dtype=np.float64)
-    return 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
-
-
-def normed_matmul(x, g, w, eps, rb):
-    """N(x, g) W^T = s(x) * (rb(x * g) W^T): RMSNorm with gain g, its row factor taken
-    out of the product (see the layer spec above)."""
-    x = np.asarray(x, dtype=np.float64)
-    return rms_scale(x, eps) * matmul(rb(x * np.asarray(g, dtype=np.float64)), w)
 
 
 def rope(t, pos, theta):
@@ -180,6 +168,69 @@ def matmul(a, w):
     return a @ w.T
 
 
+def _rb(c):
+    return round_bf16 if c.dtype == "bf16" else (lambda t: np.asarray(t, dtype=np.float64))
+
+
+def _w(W, name):
+    return np.asarray(W[name], dtype=np.float64)
+
+
+def layer_weights(W, l):
+    """The float64 tensors of layer l (a dict with the same keys as W)."""
+    pre = f"l{l}."
+    return {k: _w(W, k) for k in W if k.startswith(pre)}
+
+
+def normed_input(x, g, eps, rb):
+    """h = bf16(RMSNorm(x) * g): the input of a normalised product."""
+    return rb(rmsnorm(x, g, eps))
+
+
+def attention_half(cfg, W, cache, l, b, x, pos):
+    """First half of layer l for sequence row b: n new rows x [n, d] at absolute
+    positions pos [n] (pos[0] = the row's cache length before them).  Appends their
+    K/V to cache layer l at pos and returns x + o W_o^T (float64)."""
+    c = OracleConfig(cfg)
+    rb = _rb(c)
+    H, hd, d = c.n_heads, c.head_dim, c.d_model
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    s0 = int(pos[0])
+    h = normed_input(x, _w(W, f"l{l}.norm1"), c.norm_eps, rb)
+    qkv = matmul(h, _w(W, f"l{l}.wqkv"))
+    q = qkv[:, :d].reshape(n, H, hd)
+    k = qkv[:, d:2 * d].reshape(n, H, hd)
+    v = qkv[:, 2 * d:].reshape(n, H, hd)
+    q = rb(rope(q, pos, c.rope_theta))
+    k = rb(rope(k, pos, c.rope_theta))
+    v = rb(v)
+    cache.k[l][b, :, s0:s0 + n] = k.transpose(1, 0, 2)
+    cache.v[l][b, :, s0:s0 + n] = v.transpose(1, 0, 2)
+    o = attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], pos)
+    return x + matmul(rb(o.reshape(n, d)), _w(W, f"l{l}.wo"))
+
+
+def ffn_half(cfg, W, l, x):
+    """Second half of layer l: x + FFN(bf16(RMSNorm(x) * g2)) for rows x [n, d]."""
+    c = OracleConfig(cfg)
+    rb = _rb(c)
+    x = np.asarray(x, dtype=np.float64)
+    h = normed_input(x, _w(W, f"l{l}.norm2"), c.norm_eps, rb)
+    if c.ffn_kind == "swiglu":
+        a = rb(silu(matmul(h, _w(W, f"l{l}.wgate"))) * matmul(h, _w(W, f"l{l}.wup")))
+        return x + matmul(a, _w(W, f"l{l}.wdown"))
+    a = rb(gelu(matmul(h, _w(W, f"l{l}.w1"))))
+    return x + matmul(a, _w(W, f"l{l}.w2"))
+
+
+def lm_head(cfg, W, x):
+    """logits = bf16(RMSNorm(x) * g_f) W_head^T for rows x [n, d]."""
+    c = OracleConfig(cfg)
+    rb = _rb(c)
+    return matmul(normed_input(x, _w(W, "norm_f"), c.norm_eps, rb), _w(W, "head"))
+
+
 def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
     """Score new tokens on top of the cache and append their K/V.
 
@@ -189,53 +240,23 @@ def forward(cfg, W, cache, tokens, n_tok=None, layers=None):
     still runs), which the timing of very large models uses.
     """
     c = OracleConfig(cfg)
-    rb = round_bf16 if c.dtype == "bf16" else (lambda t: np.asarray(t, dtype=np.float64))
     tokens = np.asarray(tokens, dtype=np.int64)
     B, M = tokens.shape
     n_tok = np.full(B, M, dtype=np.int64) if n_tok is None else np.asarray(n_tok, np.int64)
     n_layers = c.n_layers if layers is None else int(layers)
-    H, hd, d = c.n_heads, c.head_dim, c.d_model
     if np.any(cache.len + n_tok > cache.max_len):
         raise ValueError("KV cache overflow")
-    f64 = lambda name: np.asarray(W[name], dtype=np.float64)
     rows = [b for b in range(B) if n_tok[b] > 0]
-    L0 = {b: int(cache.len[b]) for b in rows}
-    pos = {b: L0[b] + np.arange(int(n_tok[b])) for b in rows}
-    E = f64("embed")
-    x = {b: E[tokens[b, :n_tok[b]]] for b in rows}
+    pos = {b: int(cache.len[b]) + np.arange(int(n_tok[b])) for b in rows}
+    E = np.asarray(W["embed"])
+    x = {b: E[tokens[b, :n_tok[b]]].astype(np.float64) for b in rows}
     for l in range(n_layers):
-        wqkv, wo = f64(f"l{l}.wqkv"), f64(f"l{l}.wo")
-        g1, g2 = f64(f"l{l}.norm1"), f64(f"l{l}.norm2")
-        if c.ffn_kind == "swiglu":
-            wg, wu, wd = f64(f"l{l}.wgate"), f64(f"l{l}.wup"), f64(f"l{l}.wdown")
-        else:
-            w1, w2 = f64(f"l{l}.w1"), f64(f"l{l}.w2")
+        Wl = layer_weights(W, l)   # float64 once per layer, shared by the rows
         for b in rows:
-            n, s0, p = int(n_tok[b]), L0[b], pos[b]
-            qkv = normed_matmul(x[b], g1, wqkv, c.norm_eps, rb)
-            q = qkv[:, :d].reshape(n, H, hd)
-            k = qkv[:, d:2 * d].reshape(n, H, hd)
-            v = qkv[:, 2 * d:].reshape(n, H, hd)
-            q = rb(rope(q, p, c.rope_theta))
-            k = rb(rope(k, p, c.rope_theta))
-            v = rb(v)
-            cache.k[l][b, :, s0:s0 + n] = k.transpose(1, 0, 2)
-            cache.v[l][b, :, s0:s0 + n] = v.transpose(1, 0, 2)
-            o = attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], p)
-            o = o.reshape(n, d)
-            xb = x[b] + matmul(rb(o), wo)
-            if c.ffn_kind == "swiglu":
-                gate = normed_matmul(xb, g2, wg, c.norm_eps, rb)
-                up = normed_matmul(xb, g2, wu, c.norm_eps, rb)
-                a = rb(silu(gate) * up)
-                xb = xb + matmul(a, wd)
-            else:
-                a = rb(gelu(normed_matmul(xb, g2, w1, c.norm_eps, rb)))
-                xb = xb + matmul(a, w2)
-            x[b] = xb
+            x[b] = ffn_half(c, Wl, l, attention_half(c, Wl, cache, l, b, x[b], pos[b]))
     logits = np.zeros((B, M, c.vocab))
-    head, gf = f64("head"), f64("norm_f")
+    Wh = {"norm_f": _w(W, "norm_f"), "head": _w(W, "head")}
     for b in rows:
-        logits[b, :n_tok[b]] = normed_matmul(x[b], gf, head, c.norm_eps, rb)
+        logits[b, :n_tok[b]] = lm_head(c, Wh, x[b])
     cache.len = cache.len + n_tok
     return logits

@@ -141,25 +141,43 @@ def test_rmsnorm_closed_form():
     np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
 
 
-def test_normed_matmul_is_rmsnorm_then_product():
-    """N(x, g) W^T: without bf16 rounding it is RMSNorm(x) * g times W^T (the row factor
-    commutes with the product); with bf16 rounding of the input it stays within the
-    rounding bound of the same product formed from bf16(RMSNorm(x) * g)."""
+def test_normed_input_closed_form():
+    """The input of a normalised product is bf16(RMSNorm(x) * g): RMSNorm of [3, -4, 0, 0]
+    (rms 2.5) with gains [1, 2, 1, 1] is [1.2, -3.2, 0, 0], which rounds to the bf16
+    values 1.203125 and -3.203125 (8 significant bits; 1.2 = 1.0011001...b)."""
+    x = np.array([[3.0, -4.0, 0.0, 0.0]])
+    g = np.array([1.0, 2.0, 1.0, 1.0])
+    h = model.normed_input(x, g, 0.0, model.round_bf16)
+    np.testing.assert_array_equal(h, [[1.203125, -3.203125, 0.0, 0.0]])
+    # the row factor scales before the one rounding: a row and the same row times 2^k
+    # (any k) normalise to the same bf16 input
     rng = np.random.default_rng(10)
-    x = rng.standard_normal((5, 96)) * rng.uniform(0.1, 30.0, (5, 1))
-    g = rng.uniform(0.5, 1.5, 96)
-    w = rng.standard_normal((40, 96)) * 0.02
-    ident = lambda t: np.asarray(t, dtype=np.float64)
-    got = model.normed_matmul(x, g, w, 1e-5, ident)
-    ref = model.rmsnorm(x, g, 1e-5) @ w.T
-    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
-    # bf16 inputs: both orders round each element once (relative error <= 2^-9), so
-    # they differ by at most 2 * 2^-9 * sum_k |RMSNorm(x)_k g_k w_nk| per output
-    gotb = model.normed_matmul(x, g, w, 1e-5, model.round_bf16)
-    other = model.round_bf16(model.rmsnorm(x, g, 1e-5)) @ w.T
-    bound = 2 * 2.0 ** -9 * (np.abs(model.rmsnorm(x, g, 1e-5)) @ np.abs(w).T) + 1e-15
-    assert np.all(np.abs(gotb - other) <= bound)
-    assert np.any(gotb != other)   # the rounding point did move
+    z = rng.standard_normal((3, 64))
+    np.testing.assert_array_equal(model.normed_input(z, np.ones(64), 0.0, model.round_bf16),
+                                  model.normed_input(z * 2.0 ** 37, np.ones(64), 0.0,
+                                                     model.round_bf16))
+
+
+def test_forward_is_the_composition_of_its_halves():
+    """forward() = embedding -> (attention half, FFN half) per layer -> LM head, row by
+    row; the halves fed the same rows reproduce its logits and its cache entries."""
+    s = micro("bf16", "swiglu")
+    W = weights(s, seed=11)
+    rng = np.random.default_rng(11)
+    ctx = rng.integers(0, s.vocab, (1, 5))
+    new = rng.integers(0, s.vocab, (1, 3))
+    c1 = model.KVCache(s, 1, 16)
+    model.forward(s, W, c1, ctx)
+    c2 = c1.copy()
+    got = model.forward(s, W, c1, new)
+    x = W["embed"][new[0]].astype(np.float64)
+    pos = 5 + np.arange(3)
+    for l in range(s.n_layers):
+        x = model.ffn_half(s, W, l, model.attention_half(s, W, c2, l, 0, x, pos))
+    np.testing.assert_array_equal(model.lm_head(s, W, x), got[0])
+    for l in range(s.n_layers):
+        np.testing.assert_array_equal(c1.k[l][0, :, :8], c2.k[l][0, :, :8])
+        np.testing.assert_array_equal(c1.v[l][0, :, :8], c2.v[l][0, :, :8])
 
 
 def test_rope_properties():

@@ -129,6 +129,61 @@ def test_top_p_ties_are_kept():
     assert np.array_equal(s > 0, [True, True, True, True, False])
 
 
+def _kept_set(l, T, top_p):
+    return sampling.transform(l, T, top_p=top_p) > 0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_top_p_threshold_margin_is_the_distance_to_the_next_membership_change(seed):
+    """top_p_threshold_margin(s, tp) is the distance from tp to the nearest top-p mass at
+    which the kept set changes, found here by bisection on the transform itself (which
+    the brute-force tests pin): the kept set is the same for every threshold within the
+    margin and differs just beyond it on one side.  Rows with tied probabilities are
+    included (ties move in and out of the kept set together)."""
+    rng = np.random.default_rng(40 + seed)
+    V = 24
+    l = rng.normal(0, 1.5, V).astype(np.float32)
+    if seed % 2:
+        l[rng.choice(V, 6, replace=False)] = l[0]   # a tied group
+    T = 1.0
+    base = sampling.transform(l, T)
+    for tp in [0.35, 0.6, 0.9]:
+        tp32 = float(np.float32(tp))
+        m = sampling.top_p_threshold_margin(base, tp32)
+        assert m > 1e-5, "the margins below are resolved to ~1e-7 only"
+        ref = _kept_set(l, T, tp32)
+        for f in (-0.98, -0.5, 0.5, 0.98):
+            t = tp32 + f * m
+            if 0.0 < t <= 1.0:
+                assert np.array_equal(_kept_set(l, T, t), ref), (tp, f, m)
+        # brute force: the nearest threshold (within [0, 1]) where the set changes
+        def changes(t):
+            return not np.array_equal(_kept_set(l, T, t), ref)
+
+        best = np.inf
+        for direction in (-1.0, 1.0):
+            lo, hi = 0.0, None
+            step = 1e-4
+            while hi is None and step < 2.0:
+                t = tp32 + direction * step
+                if not 0.0 < t <= 1.0:
+                    break
+                if changes(t):
+                    hi = step
+                else:
+                    lo, step = step, step * 1.5
+            if hi is None:
+                continue
+            for _ in range(60):
+                mid = 0.5 * (lo + hi)
+                if changes(tp32 + direction * mid):
+                    hi = mid
+                else:
+                    lo = mid
+            best = min(best, hi)
+        assert abs(best - m) <= 1e-6 * max(1.0, m) + 1e-9, (tp, best, m)
+
+
 def test_knob_order_temperature_then_top_k_then_top_p():
     rng = np.random.default_rng(5)
     l = rng.normal(0, 2, 64).astype(np.float32)
