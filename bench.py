@@ -94,20 +94,24 @@ def gemm_bytes_per_verify(shape, R):
     """Algorithmic bytes of the weight GEMMs of one forward over R rows: every weight
     once and the activation rows read; outputs: q / K / V / FFN activations in the
     element type (QKV, up), the residual rows read and written in fp32 plus the next
-    product's input and its per-16-column sums of squares (O-proj, down), fp32 logits
-    (LM head).  Normalised products also read their rows' sums of squares."""
+    normalised product's fp32 input x * g and its per-16-column sums of squares (O-proj,
+    down), fp32 logits (LM head).  A normalised product reads the fp32 x * g rows and
+    their sums of squares when it forms its input itself (R <= 16), else the bf16 rows
+    of the normalise pass."""
     d, F, V, L = shape.d_model, shape.d_ffn, shape.vocab, shape.n_layers
     e = shape.elt_bytes()
     ffn_in = 2 * F if shape.ffn_kind == "swiglu" else F
     ss = R * (d // 16) * 4
-    resid_out = R * d * 4 * 2 + R * d * e + ss
-    gemms = [(3 * d, d, R * 3 * d * e + ss), (d, d, resid_out), (ffn_in, d, R * F * e + ss),
-             (d, F, resid_out)]  # (N, K, output-side bytes)
+    normed_in = R * d * 4 + ss if R <= 16 else R * d * e
+    resid_out = R * d * 4 * 3 + ss
+    # (N, K, input bytes, output bytes) of qkv, O-proj, up, down
+    gemms = [(3 * d, d, normed_in, R * 3 * d * e), (d, d, R * d * e, resid_out),
+             (ffn_in, d, normed_in, R * F * e), (d, F, R * F * e, resid_out)]
     total, n = 0, 0
-    for N, K, out in gemms:
-        total += L * (N * K * e + R * K * e + out)
+    for N, K, a_in, out in gemms:
+        total += L * (N * K * e + a_in + out)
         n += L
-    total += V * d * e + R * d * e + ss + R * V * 4
+    total += V * d * e + normed_in + R * V * 4
     n += 1
     return total, n
 

@@ -20,10 +20,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates and
- *     frees every device buffer (weights, KV arena, lengths, logits, tokens, outputs,
- *     workspace); no call allocates device memory, synchronises the device or throws.
- *   - Compute calls are asynchronous on `stream` (a hipStream_t; 0 = null stream).
- *     The caller keeps buffers alive until the stream work has finished.
+ *     frees every device buffer (model store, KV arena, lengths, logits, tokens,
+ *     outputs, workspace); no call allocates device memory or throws, and no call
+ *     waits for the device except spec_timing_read (a measurement aid).
+ *   - Calls that launch work are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     null stream).  The caller keeps buffers alive until the stream work has finished.
  *   - A handle (spec_model, spec_kv) is an opaque host object owned by the library;
  *     use one handle from one stream at a time.
  *   - Arguments the host can check are checked before anything is launched; a bad
@@ -93,43 +94,43 @@ typedef struct spec_kv spec_kv;       /* opaque */
 
 /* ------------------------------------------------------------------ model --------- */
 
-/* Number of weight pointers spec_model_create expects for `cfg`. */
+/* Number of tensors of a model of `cfg` (the canonical order of spec_model_load_weight). */
 int spec_model_n_weights(const spec_model_cfg* cfg);
 
-/* Device bytes a model of `cfg` allocates for its own copy of the weights (0 for an
+/* Bytes of the device store a model of `cfg` keeps its copy of the weights in (0 for an
  * invalid cfg). */
 size_t spec_model_bytes(const spec_model_cfg* cfg);
 
-/* Create a model: the library allocates spec_model_bytes(cfg) of device memory and
- * keeps its own copy of every tensor there, the bf16 matrices rearranged into the
- * tile order the verify GEMM streams (column tiles of 16 weight rows, each tile one
- * contiguous block in MFMA operand order), so each weight byte is read from HBM once
- * in fully used 1 KB wave loads ([ZSM] "The cost of one token is the cost of reading
- * the weights").  `weights` (host array of device pointers, or NULL) in this order:
+/* Create a model handle over a caller-owned device store of store_bytes >=
+ * spec_model_bytes(cfg) bytes (256-byte aligned; the caller frees it after
+ * spec_model_destroy).  Nothing is allocated or launched: fill the store with
+ * spec_model_load_weight, one call per tensor.  The store holds every tensor, the bf16
+ * matrices rearranged into the tile order the verify GEMM streams (column tiles of 16
+ * weight rows, each tile one contiguous block in MFMA operand order), so each weight byte
+ * is read from HBM once in fully used 1 KB wave loads ([ZSM] "The cost of one token is
+ * the cost of reading the weights"; [GC] "Why Standard Decoding Is Slow").
+ * Returns SPEC_E_INVALID for a bad shape, a null or misaligned pointer;
+ * SPEC_E_CAPACITY for a store smaller than spec_model_bytes; SPEC_E_UNSUPPORTED for a
+ * shape the kernels are not built for (bf16: head_dim 64 or 128, d_model and d_ffn
+ * multiples of 128, vocab a multiple of 16; f32: even head_dim <= 128) or a device that
+ * is not gfx950.  *out receives the handle. */
+spec_status spec_model_create(const spec_model_cfg* cfg, void* store, size_t store_bytes,
+                              spec_model** out);
+
+/* Copy tensor `index` into the model's store, asynchronously on `stream`: `src` (device,
+ * the layout below) must stay valid until the stream has passed this call.  Canonical
+ * order of the spec_model_n_weights(cfg) tensors:
  *   embed [V,d], head [V,d], norm_f [d] (fp32),
  *   then per layer: norm1 [d] (fp32), wqkv [3d,d] (rows: q heads | k heads | v heads),
  *   wo [d,d], norm2 [d] (fp32), then SwiGLU: wgate [F,d], wup [F,d], wdown [d,F]
  *   or GELU: w1 [F,d], w2 [d,F].
  * Matrices and embeddings are bf16 for SPEC_DT_BF16 and fp32 for SPEC_DT_F32, row-major
- * [out, in].  With weights given, every tensor is copied before the call returns (on
- * the null stream, which is synchronised) and the caller may free its buffers; with
- * weights == NULL the storage is left unset for spec_model_load_weight.
- * Returns SPEC_E_INVALID for a bad shape, count or null pointer; SPEC_E_UNSUPPORTED
- * for a shape the kernels are not built for (bf16: head_dim 64 or 128, d_model and
- * d_ffn multiples of 128, vocab a multiple of 16; f32: even head_dim <= 128) or a
- * device that is not gfx950; SPEC_E_CAPACITY if the device allocation fails.
- * *out receives the handle. */
-spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
-                              int n_weights, spec_model** out);
-
-/* Copy tensor `index` (canonical order above; device pointer `src` in the layout
- * given there) into the model, asynchronously on `stream` (NULL: the null stream):
- * `src` must stay valid until the stream has passed this call.  Lets a loader stage
- * one tensor at a time (peak memory: the model plus one tensor).  SPEC_E_INVALID for
- * a bad index or null pointer, SPEC_E_HIP if the copy cannot be queued. */
+ * [out, in].  A loader can stage one tensor at a time (peak memory: the store plus one
+ * tensor).  SPEC_E_INVALID for a bad index or null pointer, SPEC_E_HIP if the copy cannot
+ * be queued. */
 spec_status spec_model_load_weight(spec_model* m, int index, const void* src, void* stream);
 
-/* Free the model and its device copy of the weights. */
+/* Free the handle (host memory only; the store stays the caller's). */
 spec_status spec_model_destroy(spec_model* m);
 
 /* ------------------------------------------------------------------ KV cache ------ */
@@ -144,11 +145,13 @@ spec_status spec_model_destroy(spec_model* m);
  * in natural order. */
 size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len);
 
-/* Bind a cache to a caller-owned arena of at least spec_kv_bytes() and to a caller-
- * owned int32 length vector len[batch] (device; the number of valid positions of each
- * row; the caller initialises it, usually to 0).  Nothing is launched. */
+/* Bind a cache to a caller-owned arena of at least spec_kv_bytes() (256-byte aligned)
+ * and to a caller-owned int32 length vector len[batch] (device; the number of valid
+ * positions of each row; the caller initialises it, usually to 0).  For bf16 models one
+ * kernel is queued on `stream` that writes the RoPE table into the arena tail; the cache
+ * is usable by later work on that stream (other streams must wait for it). */
 spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, void* arena,
-                           size_t arena_bytes, int32_t* len, spec_kv** out);
+                           size_t arena_bytes, int32_t* len, void* stream, spec_kv** out);
 spec_status spec_kv_destroy(spec_kv* kv);
 
 /* Device pointer to the start of the arena's K/V element block. */
@@ -192,6 +195,27 @@ spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t*
                                 const int32_t* n_tok, int B, int M, float* logits,
                                 int32_t* row_status, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* spec_verify_forward that also exports the residual stream and the rounded activations
+ * that enter the residual updates, for parity checks of each half-layer against a
+ * reference fed the same rows:
+ *   resid    [2 * n_layers + 1, B * M, d] fp32 out: entry 0 the embedded rows, entry
+ *            2l + 1 the rows after layer l's attention half (x + o W_o^T), entry 2l + 2
+ *            after its FFN half (x + a W_down^T);
+ *   q        [n_layers, B * M, d] out or NULL: each layer's rotated queries as attention
+ *            takes them (bf16 for bf16 models, fp32 for f32 models);
+ *   attn_out [n_layers, B * M, d] out or NULL: o of each layer (the attention output as
+ *            the O product takes it: bf16 for bf16 models, fp32 for f32 models);
+ *   ffn_act  [n_layers, B * M, d_ffn] out or NULL: a of each layer (the FFN activation as
+ *            the down product takes it, same element type);
+ *   rows j >= n_tok[b] of a sequence hold unspecified values.
+ * Same arguments, results and errors as spec_verify_forward otherwise (resid NULL:
+ * SPEC_E_INVALID). */
+spec_status spec_verify_forward_trace(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                                      const int32_t* n_tok, int B, int M, float* logits,
+                                      int32_t* row_status, float* resid, void* q,
+                                      void* attn_out, void* ffn_act, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /* One draft step ([ZSM] "The algorithm": the draft generates K tokens autoregressively;
  * [CANON] listing, draft loop; [LENS] §2.1 step 1): a forward of the draft model over
@@ -272,9 +296,10 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
 /* Kernel timing for measurement.  While enabled, HIP events are recorded on the launch
  * stream immediately before and after every weight-GEMM launch and every attention
  * launch (split-KV kernel + merge) of spec_verify_forward / spec_draft_step.
- * spec_timing_read waits for the recorded events, returns the summed elapsed times
- * (ms) and launch counts since the last read, and clears them.  Events are created
- * on first use and reused; timing adds the event records to the stream. */
+ * spec_timing_read waits for the recorded events (the one call that waits for the
+ * device), returns the summed elapsed times (ms) and launch counts since the last read,
+ * and clears them.  Events are created on first use and reused; timing adds the event
+ * records to the stream. */
 spec_status spec_timing_enable(int on);
 spec_status spec_timing_read(double* gemm_ms, int* gemm_launches, double* attn_ms,
                              int* attn_launches);

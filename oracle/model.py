@@ -187,10 +187,12 @@ def normed_input(x, g, eps, rb):
     return rb(rmsnorm(x, g, eps))
 
 
-def attention_half(cfg, W, cache, l, b, x, pos):
+def attention_half(cfg, W, cache, l, b, x, pos, record=None):
     """First half of layer l for sequence row b: n new rows x [n, d] at absolute
     positions pos [n] (pos[0] = the row's cache length before them).  Appends their
-    K/V to cache layer l at pos and returns x + o W_o^T (float64)."""
+    K/V to cache layer l at pos and returns x + o W_o^T (float64).  record (a dict, or
+    None) receives q [n, d], the rounded rotated queries, and o [n, d], the rounded
+    attention output the product takes."""
     c = OracleConfig(cfg)
     rb = _rb(c)
     H, hd, d = c.n_heads, c.head_dim, c.d_model
@@ -207,21 +209,29 @@ def attention_half(cfg, W, cache, l, b, x, pos):
     v = rb(v)
     cache.k[l][b, :, s0:s0 + n] = k.transpose(1, 0, 2)
     cache.v[l][b, :, s0:s0 + n] = v.transpose(1, 0, 2)
-    o = attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], pos)
-    return x + matmul(rb(o.reshape(n, d)), _w(W, f"l{l}.wo"))
+    o = rb(attend(q, cache.k[l][b, :, :s0 + n], cache.v[l][b, :, :s0 + n], pos).reshape(n, d))
+    if record is not None:
+        record["q"] = q.reshape(n, d)
+        record["o"] = o
+    return x + matmul(o, _w(W, f"l{l}.wo"))
 
 
-def ffn_half(cfg, W, l, x):
-    """Second half of layer l: x + FFN(bf16(RMSNorm(x) * g2)) for rows x [n, d]."""
+def ffn_half(cfg, W, l, x, record=None):
+    """Second half of layer l: x + FFN(bf16(RMSNorm(x) * g2)) for rows x [n, d].  record
+    (a dict, or None) receives a, the rounded activation the down product takes."""
     c = OracleConfig(cfg)
     rb = _rb(c)
     x = np.asarray(x, dtype=np.float64)
     h = normed_input(x, _w(W, f"l{l}.norm2"), c.norm_eps, rb)
     if c.ffn_kind == "swiglu":
         a = rb(silu(matmul(h, _w(W, f"l{l}.wgate"))) * matmul(h, _w(W, f"l{l}.wup")))
-        return x + matmul(a, _w(W, f"l{l}.wdown"))
-    a = rb(gelu(matmul(h, _w(W, f"l{l}.w1"))))
-    return x + matmul(a, _w(W, f"l{l}.w2"))
+        w_out = _w(W, f"l{l}.wdown")
+    else:
+        a = rb(gelu(matmul(h, _w(W, f"l{l}.w1"))))
+        w_out = _w(W, f"l{l}.w2")
+    if record is not None:
+        record["a"] = a
+    return x + matmul(a, w_out)
 
 
 def lm_head(cfg, W, x):

@@ -24,7 +24,7 @@ SYMBOLS = [
     "spec_model_destroy", "spec_kv_bytes",
     "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_import", "spec_kv_export",
     "spec_kv_rollback",
-    "spec_workspace_bytes", "spec_verify_forward", "spec_draft_step",
+    "spec_workspace_bytes", "spec_verify_forward", "spec_verify_forward_trace", "spec_draft_step",
     "spec_accept_workspace_bytes", "spec_accept_resample", "spec_verify_tokens",
     "spec_status_str", "spec_last_hip_error", "spec_abi_version", "spec_timing_enable",
     "spec_timing_read",
@@ -79,11 +79,11 @@ def load(path=None):
     sig = {
         "spec_model_n_weights": (I32, [cfgp]),
         "spec_model_bytes": (SZ, [cfgp]),
-        "spec_model_create": (I32, [cfgp, ctypes.POINTER(P), I32, ctypes.POINTER(P)]),
+        "spec_model_create": (I32, [cfgp, P, SZ, ctypes.POINTER(P)]),
         "spec_model_load_weight": (I32, [P, I32, P, P]),
         "spec_model_destroy": (I32, [P]),
         "spec_kv_bytes": (SZ, [cfgp, I32, I32]),
-        "spec_kv_create": (I32, [cfgp, I32, I32, P, SZ, P, ctypes.POINTER(P)]),
+        "spec_kv_create": (I32, [cfgp, I32, I32, P, SZ, P, P, ctypes.POINTER(P)]),
         "spec_kv_destroy": (I32, [P]),
         "spec_kv_data": (P, [P]),
         "spec_kv_import": (I32, [P, P, I32, P]),
@@ -91,6 +91,7 @@ def load(path=None):
         "spec_kv_rollback": (I32, [P, P, P]),
         "spec_workspace_bytes": (SZ, [cfgp, I32, I32, I32]),
         "spec_verify_forward": (I32, [P, P, P, P, I32, I32, P, P, P, SZ, P]),
+        "spec_verify_forward_trace": (I32, [P, P, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P]),
         "spec_draft_step": (I32, [P, P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P, SZ,
                                   P]),
         "spec_accept_workspace_bytes": (SZ, [I32, I32]),
@@ -135,28 +136,30 @@ def _alloc(nbytes, device):
 
 
 class Model:
-    """A model holding its own device copy of the weights.
+    """A model over a device store this object allocates (torch) and owns.
 
     weights: dict name -> device tensor (canonical names and shapes of the shape), copied
-    (and, for bf16 matrices, rearranged into GEMM tiles) at construction; the caller may
-    drop them afterwards.  weights=None allocates the storage only: fill it tensor by
-    tensor with ``load_weight`` (a loader's peak memory is then the model plus one
-    tensor)."""
+    into the store (bf16 matrices rearranged into GEMM tiles) on `stream`, in stream order:
+    the caller may drop them afterwards (torch reuses freed memory in stream order).
+    weights=None leaves the store unset: fill it tensor by tensor with ``load_weight`` (a
+    loader's peak memory is then the store plus one tensor)."""
 
-    def __init__(self, shape: "synth.ModelShape", weights=None):
+    def __init__(self, shape: "synth.ModelShape", weights=None, device="cuda", stream=None):
         lib = load()
         self.shape = shape
         self.cfg = ModelCfg.from_shape(shape)
         self.names = shape.weight_names()
+        n = lib.spec_model_bytes(ctypes.byref(self.cfg))
+        if n == 0:
+            raise SpecError(SPEC_E_INVALID, "spec_model_bytes")
+        self.store = _alloc(n, device)
         h = P()
-        if weights is None:
-            arr, n = None, 0
-        else:
-            ts = [weights[nm].contiguous() for nm in self.names]
-            arr, n = (P * len(ts))(*[t.data_ptr() for t in ts]), len(ts)
-        _check(lib.spec_model_create(ctypes.byref(self.cfg), arr, n, ctypes.byref(h)),
-               "spec_model_create")
+        _check(lib.spec_model_create(ctypes.byref(self.cfg), _ptr(self.store), n,
+                                     ctypes.byref(h)), "spec_model_create")
         self.handle = h
+        if weights is not None:
+            for nm in self.names:
+                self.load_weight(nm, weights[nm], stream)
 
     def load_weight(self, name, tensor, stream=None):
         """Copy one tensor (canonical name) into the model on `stream`; the tensor must
@@ -180,7 +183,7 @@ class Model:
 class KVCache:
     """A KV arena + lengths for `batch` rows of up to `max_len` positions."""
 
-    def __init__(self, shape: "synth.ModelShape", batch, max_len, device="cuda"):
+    def __init__(self, shape: "synth.ModelShape", batch, max_len, device="cuda", stream=None):
         lib = load()
         self.shape = shape
         self.cfg = ModelCfg.from_shape(shape)
@@ -192,7 +195,8 @@ class KVCache:
         self.len = torch.zeros(batch, dtype=torch.int32, device=device)
         h = P()
         _check(lib.spec_kv_create(ctypes.byref(self.cfg), batch, max_len, _ptr(self.arena), n,
-                                  _ptr(self.len), ctypes.byref(h)), "spec_kv_create")
+                                  _ptr(self.len), _stream(stream), ctypes.byref(h)),
+               "spec_kv_create")
         self.handle = h
 
     def __del__(self):
@@ -237,6 +241,20 @@ def verify_forward(model: Model, kv: KVCache, tokens, logits, ws, n_tok=None, ro
     _check(load().spec_verify_forward(model.handle, kv.handle, _ptr(tokens), _ptr(n_tok), B, M,
                                       _ptr(logits), _ptr(row_status), _ptr(ws), ws.numel(),
                                       _stream(stream)), "spec_verify_forward")
+
+
+def verify_forward_trace(model: Model, kv: KVCache, tokens, logits, resid, ws, q=None,
+                         attn_out=None, ffn_act=None, n_tok=None, row_status=None, stream=None):
+    """verify_forward that also fills resid [2L+1, B*M, d] fp32 with the residual stream
+    after the embedding and after each half of every layer, and optionally q and attn_out
+    [L, B*M, d] and ffn_act [L, B*M, F] (the model's activation type) with each layer's
+    rotated queries, rounded attention output and FFN activation."""
+    B, M = tokens.shape
+    _check(load().spec_verify_forward_trace(model.handle, kv.handle, _ptr(tokens), _ptr(n_tok),
+                                            B, M, _ptr(logits), _ptr(row_status), _ptr(resid),
+                                            _ptr(q), _ptr(attn_out), _ptr(ffn_act), _ptr(ws),
+                                            ws.numel(), _stream(stream)),
+           "spec_verify_forward_trace")
 
 
 def draft_step(model: Model, kv: KVCache, in_tok, n_in, step, knobs, seed, rnd, x_tilde,

@@ -21,6 +21,19 @@ __host__ __device__ inline size_t act_index(int r, int k, int K) {
          (k & 7);
 }
 
+// fp32 rows of a normalised product's input (x * g, before the row factor) in the same
+// tiling: tile mt, step js, slice s and half h (columns 8 g + 4 h .. + 4 of each 8-column
+// group) form one 1 KB block, in which row 16 mt + n's four floats of group g sit at
+// position 4 n + g.  A lane's 32 bytes of a slice are then two 16-byte loads, each wave
+// load one contiguous kilobyte.  A tensor of R rows and K columns spans
+// ceil(R / 16) * 16 * K floats.
+__host__ __device__ inline size_t act32_index(int r, int k, int K) {
+  return (((((size_t)(r >> 4) * (size_t)(K >> 7) + (size_t)(k >> 7)) * 4 + ((k >> 5) & 3)) * 2 +
+           ((k >> 2) & 1)) * 64 +
+          (((r & 15) << 2) | ((k >> 3) & 3))) * 4 +
+         (k & 3);
+}
+
 // rows of an activation buffer: R rounded up to whole 16-row tiles
 __host__ __device__ inline int act_rows(int R) { return (R + 15) / 16 * 16; }
 

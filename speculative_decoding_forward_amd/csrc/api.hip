@@ -97,6 +97,7 @@ struct FwdWS {
   unsigned* counters; // completion counters: [B*H] attention + 1 GEMM
   int n_counters;
   float* x;           // residual stream [R, d] fp32
+  float* xg;          // bf16: x * g of the next normalised product (act32_index order)
   void* h;            // normed activations [R, d]
   void* a;            // FFN activations [R, F]
   float* y;           // fp32 models: GEMM outputs [R, max(3d, 2F)]
@@ -134,6 +135,7 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.n_counters = B * c.n_heads * attn_groups(M) * kAttnCounterStride + 64;
   w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
+  w.xg = (float*)take(c.dtype == SPEC_DT_BF16 ? (size_t)act_rows(R) * d * 4 : 0);
   // the GEMMs' bf16 inputs in the packed activation order (whole 16-row tiles)
   w.h = take((size_t)act_rows(R) * d * e);
   w.a = take((size_t)act_rows(R) * F * e);
@@ -150,6 +152,14 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.total = off;
   return w;
 }
+
+// Parity-check exports of a traced forward (spec_verify_forward_trace).
+struct Trace {
+  float* resid;    // [2L+1][R][d]
+  void* q;         // [L][R][d] activation type, or NULL
+  void* attn_out;  // [L][R][d] activation type, or NULL
+  void* ffn_act;   // [L][R][F] activation type, or NULL
+};
 
 // Kernel timing (measurement only): start/stop events attached to the dispatch packets
 // of GEMM and attention launches (hipExtLaunchKernelGGL), so no extra commands are
@@ -186,14 +196,38 @@ Ev timed(std::vector<std::pair<int, int>>& list) {
   return ev;
 }
 
+// Residual-stream trace (parity checks): copies of x [R, d] after the embedding and after
+// each half of every layer, trace[0 .. 2L].
+#define SPEC_TRACE(idx)                                                                    \
+  do {                                                                                     \
+    if (trace)                                                                             \
+      SPEC_LAUNCH(hipMemcpyAsync(trace->resid + (size_t)(idx) * R * d, w.x,                \
+                                 (size_t)R * d * 4, hipMemcpyDeviceToDevice, s));          \
+  } while (0)
+// the layer's rotated queries (natural order already)
+#define SPEC_TRACE_Q(l)                                                                    \
+  do {                                                                                     \
+    if (trace && trace->q)                                                                 \
+      SPEC_LAUNCH(hipMemcpyAsync((char*)trace->q + (size_t)(l) * R * d * e, w.q,           \
+                                 (size_t)R * d * e, hipMemcpyDeviceToDevice, s));          \
+  } while (0)
+// the layer's rounded attention output / FFN activation in natural row order
+#define SPEC_TRACE_ACT(dst, l, src, width)                                                  \
+  do {                                                                                     \
+    if (trace && trace->dst)                                                               \
+      SPEC_LAUNCH(launch_trace_act(c.dtype, src, R, width,                                 \
+                                   (char*)trace->dst + (size_t)(l) * R * (width) * e, s)); \
+  } while (0)
+
 spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
-                        const FwdWS& w, hipStream_t s) {
+                        const FwdWS& w, hipStream_t s, const Trace* trace) {
   const spec_model_cfg& c = m->cfg;
   const int dt = c.dtype;
   const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   SPEC_LAUNCH(launch_embed(m->embed, dt, w.tok_eff, R, d, w.x, s));
+  SPEC_TRACE(0);
   const int swiglu = c.ffn_kind == SPEC_FFN_SWIGLU;
   for (int l = 0; l < c.n_layers; ++l) {
     const spec_model::Layer& L = m->layers[l];
@@ -205,13 +239,16 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
                                 3 * d, d, w.y, 0, w.rowscale, nullptr, M, s, e1.e0, e1.e1));
     SPEC_LAUNCH(launch_rope_append(dt, w.y, B, M, H, hd, c.rope_theta, w.pos0, w.ntok_eff, w.q,
                                    kl, vl, kv->row_stride, kv->head_stride, kv->max_len, s));
+    SPEC_TRACE_Q(l);
     Ev e2 = timed(g_timing.attn);
     SPEC_LAUNCH(launch_attention_f32((const float*)w.q, (const float*)kl, (const float*)vl,
                                      kv->row_stride, kv->head_stride, B, M, H, hd, w.pos0,
                                      w.ntok_eff, kv->max_len, (float*)w.att, s, e2.e0, e2.e1));
+    SPEC_TRACE_ACT(attn_out, l, w.att, d);
     Ev e3 = timed(g_timing.gemm);
     SPEC_LAUNCH(launch_gemm_f32((const float*)w.att, (const float*)L.wo, nullptr, d, R, d, d,
                                 w.x, 1, nullptr, nullptr, M, s, e3.e0, e3.e1));
+    SPEC_TRACE(2 * l + 1);
     SPEC_LAUNCH(launch_norm_input(w.x, L.norm2, R, d, c.norm_eps, (float*)w.h, w.rowscale, s));
     Ev e4 = timed(g_timing.gemm);
     if (swiglu)
@@ -222,9 +259,11 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
       SPEC_LAUNCH(launch_gemm_f32((const float*)w.h, (const float*)L.w_up, nullptr, F, R, F, d,
                                   w.y, 0, w.rowscale, nullptr, M, s, e4.e0, e4.e1));
     SPEC_LAUNCH(launch_act(dt, c.ffn_kind, w.y, R, F, w.a, s));
+    SPEC_TRACE_ACT(ffn_act, l, w.a, F);
     Ev e5 = timed(g_timing.gemm);
     SPEC_LAUNCH(launch_gemm_f32((const float*)w.a, (const float*)L.w_down, nullptr, d, R, d, F,
                                 w.x, 1, nullptr, nullptr, M, s, e5.e0, e5.e1));
+    SPEC_TRACE(2 * l + 2);
   }
   SPEC_LAUNCH(launch_norm_input(w.x, m->norm_f, R, d, c.norm_eps, (float*)w.h, w.rowscale, s));
   Ev e6 = timed(g_timing.gemm);
@@ -233,20 +272,25 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
   return SPEC_OK;
 }
 
-// bf16 models: 5 kernels per layer.
-//   QKV GEMM (row factor, RoPE, q out, K/V append) -> attention (+ split merge) ->
-//   O GEMM (x += y, next input bf16(x * g2) and its sums of squares) ->
-//   up GEMM (row factor, SwiGLU / GELU) -> down GEMM (x += y, next input and sums of
-//   squares for the next layer's QKV or the LM head)
+// bf16 models: 5 kernels per layer (up to 3 more with several row tiles).
+//   QKV GEMM (normalised input, RoPE, q out, K/V append) -> attention (+ split merge) ->
+//   O GEMM (x += y, next input x * g2 and its sums of squares) -> up GEMM (normalised
+//   input, SwiGLU / GELU) -> down GEMM (x += y, next input and sums of squares for the
+//   next layer's QKV or the LM head).
+// A normalised product takes bf16(RMSNorm(x) * g): with one row tile (R <= 16) the GEMM
+// forms it from the fp32 x * g rows and the partial sums; with more rows a normalise
+// pass writes it first (the same arithmetic, so a row's product does not depend on the
+// number of rows in the call).
 spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
-                         const FwdWS& w, hipStream_t s) {
+                         const FwdWS& w, hipStream_t s, const Trace* trace) {
   const spec_model_cfg& c = m->cfg;
   const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
-  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.h, w.ss,
+  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.xg, w.ss,
                                 kv->rope, w.pos0, M, hd, kv->max_len, w.rope_rows, s));
+  SPEC_TRACE(0);
   GemmArgs base{};
   base.R = R;
   base.M = M;
@@ -261,6 +305,20 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
   base.ss_np = d / 16;
   base.eps = c.norm_eps;
+  const bool fused_norm = R <= 16;
+  // the input of a normalised product over the current x * g rows
+  auto norm_input = [&](GemmArgs& g) -> spec_status {
+    g.K = d;
+    g.lda = d;
+    if (fused_norm) {
+      g.A32 = w.xg;
+      g.ss_in = w.ss;
+    } else {
+      SPEC_LAUNCH(launch_norm_pack(w.xg, w.ss, R, d, c.norm_eps, (uint16_t*)w.h, s));
+      g.A = (const uint16_t*)w.h;
+    }
+    return SPEC_OK;
+  };
   for (int l = 0; l < c.n_layers; ++l) {
     const spec_model::Layer& L = m->layers[l];
     uint16_t* kl = (uint16_t*)((char*)kv->data + (size_t)l * kv->layer_stride * e);
@@ -268,18 +326,16 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
     {
       GemmArgs g = base;
       g.mode = EPI_QKV_ROPE;
-      g.A = (const uint16_t*)w.h;
-      g.lda = d;
+      if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
       g.W = (const uint16_t*)L.wqkv;
       g.N = g.N1 = 3 * d;
-      g.K = d;
       g.q_out = (uint16_t*)w.q;
       g.kc = kl;
       g.vc = vl;
-      g.ss_in = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
+    SPEC_TRACE_Q(l);
     {
       Ev ev = timed(g_timing.attn);
       SPEC_LAUNCH(launch_attention_bf16((const uint16_t*)w.q, kl, vl, kv->row_stride,
@@ -287,6 +343,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
                                         w.part, attn_counters, kv->max_len,
                                         (uint16_t*)w.att, s, ev.e0, ev.e1));
     }
+    SPEC_TRACE_ACT(attn_out, l, w.att, d);
     {
       GemmArgs g = base;
       g.mode = EPI_RESID;
@@ -297,18 +354,16 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.K = d;
       g.x = w.x;
       g.gain = L.norm2;
-      g.h_out = (uint16_t*)w.h;
+      g.xg_out = w.xg;
       g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
+    SPEC_TRACE(2 * l + 1);
     {
       GemmArgs g = base;
-      g.A = (const uint16_t*)w.h;
-      g.lda = d;
-      g.K = d;
+      if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
       g.act_out = (uint16_t*)w.a;
-      g.ss_in = w.ss;
       g.W = (const uint16_t*)L.w_up;
       if (c.ffn_kind == SPEC_FFN_SWIGLU) {
         g.mode = EPI_SWIGLU;
@@ -321,6 +376,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
+    SPEC_TRACE_ACT(ffn_act, l, w.a, F);
     {
       GemmArgs g = base;
       g.mode = EPI_RESID;
@@ -331,37 +387,38 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.K = F;
       g.x = w.x;
       g.gain = l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f;
-      g.h_out = (uint16_t*)w.h;
+      g.xg_out = w.xg;
       g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
+    SPEC_TRACE(2 * l + 2);
   }
   GemmArgs g = base;
   g.mode = EPI_STORE;
-  g.A = (const uint16_t*)w.h;
-  g.lda = d;
+  if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
   g.W = (const uint16_t*)m->head;
   g.N = g.N1 = V;
-  g.K = d;
-  g.ss_in = w.ss;
   g.C = logits;
   g.ldc = V;
   Ev ev = timed(g_timing.gemm);
   SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
   return SPEC_OK;
 }
+#undef SPEC_TRACE
+#undef SPEC_TRACE_ACT
+#undef SPEC_TRACE_Q
 
 // The forward pass shared by the verify call, draft steps and prefill chunks.
 spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
                     const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
                     int record_base, const FwdWS& w, hipStream_t s,
-                    const DraftSrc* ds = nullptr) {
+                    const DraftSrc* ds = nullptr, const Trace* trace = nullptr) {
   SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, m->cfg.vocab, kv->len, kv->base, record_base,
                           kv->max_len, w.pos0, w.ntok_eff, w.tok_eff, row_status, w.counters,
                           w.n_counters, ds, s));
-  if (m->cfg.dtype == SPEC_DT_BF16) return forward_bf16(m, kv, B, M, logits, w, s);
-  return forward_f32(m, kv, B, M, logits, w, s);
+  if (m->cfg.dtype == SPEC_DT_BF16) return forward_bf16(m, kv, B, M, logits, w, s, trace);
+  return forward_f32(m, kv, B, M, logits, w, s, trace);
 }
 
 bool kv_matches(const spec_model* m, const spec_kv* kv) {
@@ -374,7 +431,7 @@ bool kv_matches(const spec_model* m, const spec_kv* kv) {
 
 extern "C" {
 
-int spec_abi_version(void) { return 1; }
+int spec_abi_version(void) { return 2; }
 
 int spec_last_hip_error(void) { return g_last_hip_error.load(); }
 
@@ -458,35 +515,25 @@ size_t spec_model_bytes(const spec_model_cfg* cfg) {
   return model_layout(*cfg, nullptr);
 }
 
-spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weights,
-                              int n_weights, spec_model** out) {
-  if (!cfg_valid(cfg) || !out) return SPEC_E_INVALID;
-  if (weights) {
-    if (n_weights != spec_model_n_weights(cfg)) return SPEC_E_INVALID;
-    for (int i = 0; i < n_weights; ++i)
-      if (!weights[i]) return SPEC_E_INVALID;
-  }
+spec_status spec_model_create(const spec_model_cfg* cfg, void* store, size_t store_bytes,
+                              spec_model** out) {
+  if (!cfg_valid(cfg) || !store || !out) return SPEC_E_INVALID;
+  if (((uintptr_t)store) % kAlign) return SPEC_E_INVALID;
   if (!cfg_supported(cfg)) return SPEC_E_UNSUPPORTED;
-  if (!device_is_gfx950()) return SPEC_E_UNSUPPORTED;
   const int n = spec_model_n_weights(cfg);
   std::vector<TensorSlot> slots(n);
   const size_t bytes = model_layout(*cfg, slots.data());
+  if (store_bytes < bytes) return SPEC_E_CAPACITY;
+  if (!device_is_gfx950()) return SPEC_E_UNSUPPORTED;
   spec_model* m = new (std::nothrow) spec_model;
   if (!m) return SPEC_E_INVALID;
   m->cfg = *cfg;
   m->layers = new (std::nothrow) spec_model::Layer[cfg->n_layers];
-  m->store = nullptr;
+  m->store = store;
   m->store_bytes = bytes;
   if (!m->layers) {
     delete m;
     return SPEC_E_INVALID;
-  }
-  hipError_t err = hipMalloc(&m->store, bytes);
-  if (err != hipSuccess) {
-    g_last_hip_error.store((int)err);
-    delete[] m->layers;
-    delete m;
-    return SPEC_E_CAPACITY;
   }
   char* base = (char*)m->store;
   int i = 0;
@@ -507,21 +554,6 @@ spec_status spec_model_create(const spec_model_cfg* cfg, const void* const* weig
       if (cfg->dtype != SPEC_DT_BF16) L.w_up2 = up;
     }
     L.w_down = at();
-  }
-  if (weights) {
-    for (int k = 0; k < n; ++k) {
-      const spec_status st = spec_model_load_weight(m, k, weights[k], nullptr);
-      if (st != SPEC_OK) {
-        spec_model_destroy(m);
-        return st;
-      }
-    }
-    err = hipStreamSynchronize(nullptr);
-    if (err != hipSuccess) {
-      g_last_hip_error.store((int)err);
-      spec_model_destroy(m);
-      return SPEC_E_HIP;
-    }
   }
   *out = m;
   return SPEC_OK;
@@ -552,7 +584,6 @@ spec_status spec_model_load_weight(spec_model* m, int index, const void* src, vo
 
 spec_status spec_model_destroy(spec_model* m) {
   if (!m) return SPEC_E_INVALID;
-  if (m->store) hipFree(m->store);
   delete[] m->layers;
   delete m;
   return SPEC_OK;
@@ -572,7 +603,7 @@ size_t spec_kv_bytes(const spec_model_cfg* cfg, int batch, int max_len) {
 }
 
 spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, void* arena,
-                           size_t arena_bytes, int32_t* len, spec_kv** out) {
+                           size_t arena_bytes, int32_t* len, void* stream, spec_kv** out) {
   if (!cfg_valid(cfg) || batch < 1 || max_len < 1 || !arena || !len || !out)
     return SPEC_E_INVALID;
   if (((uintptr_t)arena) % 256) return SPEC_E_INVALID;
@@ -594,21 +625,10 @@ spec_status spec_kv_create(const spec_model_cfg* cfg, int batch, int max_len, vo
   kv->base = (int32_t*)((char*)arena + align_up(n * elt_bytes(*cfg)));
   kv->rope = nullptr;
   if (cfg->dtype == SPEC_DT_BF16) {
-    // rotation factors in fp64, evaluated once on the host: angle pos * theta^(-2i/hd)
+    // rotation factors in fp64, written into the arena tail on the caller's stream
     kv->rope = (double*)((char*)kv->base + align_up((size_t)batch * 4));
-    const int half = cfg->head_dim / 2;
-    std::vector<double> tab((size_t)max_len * half * 2);
-    for (int i = 0; i < half; ++i) {
-      const double inv_freq =
-          std::pow((double)cfg->rope_theta, -2.0 * (double)i / (double)cfg->head_dim);
-      for (int p = 0; p < max_len; ++p) {
-        const double a = (double)p * inv_freq;
-        tab[((size_t)p * half + i) * 2] = std::cos(a);
-        tab[((size_t)p * half + i) * 2 + 1] = std::sin(a);
-      }
-    }
-    const hipError_t err =
-        hipMemcpy(kv->rope, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice);
+    const hipError_t err = launch_rope_table(kv->rope, max_len, cfg->head_dim,
+                                             (double)cfg->rope_theta, (hipStream_t)stream);
     if (err != hipSuccess) {
       g_last_hip_error.store((int)err);
       delete kv;
@@ -681,6 +701,22 @@ spec_status spec_verify_forward(const spec_model* m, spec_kv* kv, const int32_t*
   const FwdWS w = fwd_layout(m->cfg, B, M, kv->max_len, (char*)ws);
   if (ws_bytes < w.total) return SPEC_E_CAPACITY;
   return forward(m, kv, tokens, n_tok, B, M, logits, row_status, 1, w, (hipStream_t)stream);
+}
+
+spec_status spec_verify_forward_trace(const spec_model* m, spec_kv* kv, const int32_t* tokens,
+                                      const int32_t* n_tok, int B, int M, float* logits,
+                                      int32_t* row_status, float* resid, void* q,
+                                      void* attn_out, void* ffn_act, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!m || !kv || !tokens || !logits || !ws || !resid) return SPEC_E_INVALID;
+  if (B < 1 || B > kv->batch || M < 1 || M > 64) return SPEC_E_INVALID;
+  if (!kv_matches(m, kv)) return SPEC_E_INVALID;
+  if (((uintptr_t)ws) % 256) return SPEC_E_INVALID;
+  const FwdWS w = fwd_layout(m->cfg, B, M, kv->max_len, (char*)ws);
+  if (ws_bytes < w.total) return SPEC_E_CAPACITY;
+  const Trace tr{resid, q, attn_out, ffn_act};
+  return forward(m, kv, tokens, n_tok, B, M, logits, row_status, 1, w, (hipStream_t)stream,
+                 nullptr, &tr);
 }
 
 spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t* in_tok,

@@ -12,9 +12,9 @@
 
 struct spec_model {
   spec_model_cfg cfg;
-  // The model owns one device allocation holding its copy of every tensor: bf16
-  // matrices packed into GEMM tiles, the rest (embedding, norm gains, fp32 matrices)
-  // stored as given.
+  // The caller's device store (spec_model_bytes) holds the model's copy of every tensor:
+  // bf16 matrices packed into GEMM tiles, the rest (embedding, norm gains, fp32
+  // matrices) stored as given.
   void* store;
   size_t store_bytes;
   const void* embed;   // [V, d] as given
@@ -53,7 +53,7 @@ struct SamplingKnobs {
 namespace specdec {
 
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float* x, void* h, float* ss, const double* rope,
+                             const float* g, float* x, float* xg, float* ss, const double* rope,
                              const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
                              hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
@@ -122,6 +122,10 @@ hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t*
                                uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
                                float* q_logits, hipStream_t s);
 hipError_t launch_rollback(int32_t* len, const int32_t* new_len, int B, hipStream_t s);
+hipError_t launch_rope_table(double* tab, int max_len, int hd, double theta, hipStream_t s);
+// R rows of width K of an activation buffer (bf16: the packed order; fp32: natural) into
+// natural row-major order (parity-check exports)
+hipError_t launch_trace_act(int dtype, const void* src, int R, int K, void* dst, hipStream_t s);
 hipError_t launch_verify_tokens(const int32_t* pending, const int32_t* n_pending,
                                 const int32_t* x_tilde, int B, int K, int32_t* tokens,
                                 hipStream_t s);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = binding.load()
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     assert lib.spec_status_str(0) == b"ok"
     assert lib.spec_status_str(-3) == b"buffer too small"
 
@@ -65,6 +65,27 @@ def test_argument_checks_launch_nothing():
                                    None) == binding.SPEC_E_INVALID
     assert lib.spec_kv_rollback(None, None, None) == binding.SPEC_E_INVALID
     assert lib.spec_model_destroy(None) == binding.SPEC_E_INVALID
+    assert lib.spec_verify_forward_trace(None, None, None, None, 1, 1, None, None, None, None,
+                                         None, None, None, 0, None) == binding.SPEC_E_INVALID
+    # model and cache binding: caller-owned buffers are checked on the host (these
+    # addresses are never dereferenced: every check fails before anything is touched)
+    cfg = binding.ModelCfg.from_shape(synth.WORKLOADS["small"].target)
+    h = ctypes.c_void_p()
+    need = lib.spec_model_bytes(ctypes.byref(cfg))
+    assert need > 0 and need % 256 == 0
+    assert lib.spec_model_create(ctypes.byref(cfg), None, need, ctypes.byref(h)) == \
+        binding.SPEC_E_INVALID
+    assert lib.spec_model_create(ctypes.byref(cfg), ctypes.c_void_p(4096 + 16), need,
+                                 ctypes.byref(h)) == binding.SPEC_E_INVALID
+    assert lib.spec_model_create(ctypes.byref(cfg), ctypes.c_void_p(4096), need - 256,
+                                 ctypes.byref(h)) == binding.SPEC_E_CAPACITY
+    kvb = lib.spec_kv_bytes(ctypes.byref(cfg), 2, 64)
+    assert lib.spec_kv_create(ctypes.byref(cfg), 2, 64, ctypes.c_void_p(4096 + 8), kvb,
+                              ctypes.c_void_p(4096), None, ctypes.byref(h)) == \
+        binding.SPEC_E_INVALID
+    assert lib.spec_kv_create(ctypes.byref(cfg), 2, 64, ctypes.c_void_p(4096), kvb - 256,
+                              ctypes.c_void_p(4096), None, ctypes.byref(h)) == \
+        binding.SPEC_E_CAPACITY
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -1,7 +1,8 @@
 """GPU parity of spec_verify_forward (the verify pass) against the oracle forward.
 
-Tolerances: logits within 1e-4 abs for fp32 models and 1e-2 abs for bf16 models (fp32
-accumulation).  Cache contents of the appended positions are compared too.
+Tolerances: logits within 1e-4 abs for fp32 models and 1e-2 abs (mean 1e-3) for bf16
+models (fp32 accumulation).  Cache contents of the appended positions are compared too.
+Full-depth parity, half-layer by half-layer, is in tests/test_gpu_layers.py.
 """
 import dataclasses
 
@@ -13,6 +14,7 @@ from oracle import model as omodel
 from speculative_decoding_forward_amd import binding, synth
 
 from helpers import DEV, to_dev
+from helpers_trace import check_head, check_layers, end_to_end, traced_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -162,127 +164,40 @@ def test_rollback():
     assert np.array_equal(kv.len.cpu().numpy(), [4, 10])
 
 
-def _matmul_f32_ksteps(a, w, step=128):
-    """a @ w.T accumulated in float32 over consecutive 128-wide K steps (the structure
-    of an fp32-accumulating K loop)."""
-    a32, w32 = np.asarray(a, np.float32), np.asarray(w, np.float32)
-    acc = None
-    for k0 in range(0, a32.shape[-1], step):
-        part = a32[..., k0:k0 + step] @ w32[:, k0:k0 + step].T
-        acc = part if acc is None else (acc + part).astype(np.float32)
-    return acc.astype(np.float64)
-
-
-def oracle_spread(fn):
-    """Run an oracle computation as written and in four other evaluations that are just
-    as correct for a bf16 model with fp32 accumulation: every bf16 rounding taken from
-    the float32-rounded value; every value perturbed by a seeded relative 2^-18 before
-    its bf16 rounding (the size of fp32 accumulation error over a few thousand terms,
-    sqrt(K) * 2^-24); every matrix product accumulated in float32; and every product
-    accumulated in float32 over 128-wide K steps.  The largest elementwise difference
-    from the first run is the spread that rounding and accumulation order alone produce:
-    a value that lands on the other side of a bf16 rounding boundary moves by one bf16
-    step, and such moves cascade through the layers."""
-    o1 = fn()
-    orig_rb, orig_mm = omodel.round_bf16, omodel.matmul
-    try:
-        omodel.round_bf16 = lambda x: orig_rb(np.asarray(x, np.float64).astype(np.float32))
-        o2 = fn()
-        rng = np.random.default_rng(12345)
-
-        def rb_perturbed(x):
-            x = np.asarray(x, np.float64)
-            return orig_rb(x * (1.0 + 2.0 ** -18 * rng.uniform(-1.0, 1.0, x.shape)))
-
-        omodel.round_bf16 = rb_perturbed
-        o5 = fn()
-    finally:
-        omodel.round_bf16 = orig_rb
-    try:
-        omodel.matmul = lambda a, w: (np.asarray(a, np.float32) @
-                                      np.asarray(w, np.float32).T).astype(np.float64)
-        o3 = fn()
-        omodel.matmul = _matmul_f32_ksteps
-        o4 = fn()
-    finally:
-        omodel.matmul = orig_mm
-    return o1, np.max(np.stack([np.abs(o - o1) for o in (o2, o3, o4, o5)]), axis=0)
-
-
-def assert_bf16_logits(g, o, spread, what):
-    """bf16 logits: max |diff| within max(1e-2, 3x the oracle's own rounding spread) and
-    mean |diff| within max(1e-3, 3x the mean spread)."""
-    err = np.abs(g - o)
-    tol_max = max(1e-2, 3 * spread.max())
-    tol_mean = max(1e-3, 3 * spread.mean())
-    print(f"{what}: max |diff| {err.max():.3e} (oracle spread {spread.max():.3e}), "
-          f"mean {err.mean():.3e} (spread {spread.mean():.3e}), scale {np.abs(o).max():.2f}")
-    assert err.max() <= tol_max and err.mean() <= tol_mean
-
-
-def synthetic_kv_case(wl_name, B, K, seed=0, layers=None, with_oracle=True):
-    """Verify pass of a workload's target (optionally only its first `layers` layers,
-    same weights, full width and vocabulary) on a cache filled with seeded values that
-    stand in for a prefilled context of the workload's length."""
-    wl = synth.WORKLOADS[wl_name]
-    shape = wl.target if layers is None else dataclasses.replace(wl.target, n_layers=layers)
-    m, Wn = setup(shape, seed=seed)
-    max_len = wl.ctx + K + 1
-    kv = binding.KVCache(shape, B, max_len)
-    fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=seed, device=DEV)
-    kv.import_(fill)
-    kv.len.fill_(wl.ctx)
-    new = synth.context_ids(seed + 9, B, K + 1, shape.vocab)
-    g, st = gpu_forward(m, kv, new)
-    o = spread = None
-    if with_oracle:
-        fill_np = fill.float().cpu().numpy()
-
-        def run():
-            oc = omodel.KVCache(shape, B, max_len)
-            oc.fill(fill_np, [wl.ctx] * B)
-            return omodel.forward(shape, Wn, oc, new)
-
-        o, spread = oracle_spread(run)
-    return g, o, spread, st
-
-
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
                                          ("small", 8, 7), ("7b", 8, 7), ("7b", 8, 3),
                                          ("7b", 5, 6), ("70b", 1, 4), ("7b", 16, 4),
                                          ("small", 12, 7)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
-    layers of the target.  Rows 6 and 5 take the one-row-tile GEMM; 32, 35 (a ragged last
-    row tile), 48 and 64 rows the K-outer GEMM with two to four row tiles where a
-    workgroup owns several column tiles, else the tile-at-a-time one; 80 and 96 rows
-    split into row blocks of at most 64 (64 + 16 and 64 + 32), each on its share of
-    the grid."""
-    g, o, spread, st = synthetic_kv_case(wl_name, B, K, layers=2)
-    assert np.all(st == 0)
-    assert_bf16_logits(g, o, spread, f"{wl_name} B={B} K={K} 2 layers")
-
-
-def test_full_depth_small():
-    """All 24 layers of the small target (context 512, K=4, B=1)."""
-    g, o, spread, st = synthetic_kv_case("small", 1, 4)
-    assert np.all(st == 0)
-    assert_bf16_logits(g, o, spread, "small 24 layers")
+    layers of the target, teacher-forced half by half (tests/helpers_trace.py), with the
+    rows' cache lengths staggered by 7 positions.  Rows 6 and 5 take the one-row-tile GEMM
+    that forms its normalised input itself; 32, 35 (a ragged last row tile), 48 and 64
+    rows the normalise pass and the K-outer GEMM with two to four row tiles where a
+    workgroup owns several column tiles, else the tile-at-a-time one; 80 and 96 rows split
+    into row blocks of at most 64 (64 + 16 and 64 + 32), each on its share of the grid."""
+    wl = synth.WORKLOADS[wl_name]
+    shape = dataclasses.replace(wl.target, n_layers=2)
+    t = traced_verify(shape, B, K + 1, [wl.ctx - 7 * b for b in range(B)], seed=0)
+    check_layers(t, [0, 1])
+    check_head(t)
+    end_to_end(t)
 
 
 @pytest.mark.parametrize("B,n_in", [(1, 2), (1, 1), (2, 1)])
 def test_draft_steps_match_oracle(B, n_in):
-    """Draft steps through the C ABI at the 7B draft's full width (2 layers, context 2048):
-    the draft logits of step 0 (n_in pending tokens at two rows; one pending token leaves
-    a padding row) and step 1 against the oracle's forward of the same tokens, and bitwise
-    equal to the verify entry point's logits for the same tokens and cache."""
+    """Draft steps through the C ABI at the 7B draft's full width (2 layers, context
+    2048): step 0 (n_in pending tokens at two rows; one pending token leaves a padding
+    row) and step 1.  Their logits are bitwise those of the traced verify entry point over
+    the same tokens and cache, whose every half-layer and LM head are checked against the
+    oracle teacher-forced."""
     wl = synth.WORKLOADS["7b"]
     shape = dataclasses.replace(wl.draft, n_layers=2)
-    m, Wn = setup(shape, seed=3, model_id=synth.DRAFT)
+    m, _ = setup(shape, seed=3, model_id=synth.DRAFT)
     K, V = 2, shape.vocab
     max_len = wl.ctx + 4
     kv = binding.KVCache(shape, B, max_len)
-    fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=3, device=DEV)
+    fill = synth.kv_fill(shape, B, max_len, wl.ctx, seed=3, model_id=synth.DRAFT, device=DEV)
     kv.import_(fill)
     kv.len.fill_(wl.ctx)
     toks = synth.context_ids(11, B, 2, V)
@@ -298,23 +213,14 @@ def test_draft_steps_match_oracle(B, n_in):
     torch.cuda.synchronize()
     assert np.array_equal(kv.len.cpu().numpy(), [wl.ctx + n_in + 1] * B)
     seq = np.concatenate([toks[:, :n_in], x_tilde.cpu().numpy()[:, :1]], axis=1)
-    fill_np = fill.float().cpu().numpy()
-
-    def run():
-        oc = omodel.KVCache(shape, B, max_len)
-        oc.fill(fill_np, [wl.ctx] * B)
-        return omodel.forward(shape, Wn, oc, seq)
-
-    o, spread = oracle_spread(run)
     g = q_logits.cpu().numpy()
-    # the same tokens through the verify entry point (the attention kernel's own merge)
-    kv2 = binding.KVCache(shape, B, max_len)
-    kv2.import_(fill)
-    kv2.len.fill_(wl.ctx)
-    gv, _ = gpu_forward(m, kv2, seq)
-    assert np.array_equal(g[:, 0], gv[:, n_in - 1]) and np.array_equal(g[:, 1], gv[:, n_in])
-    assert_bf16_logits(g[:, 0], o[:, n_in - 1], spread[:, n_in - 1], f"draft step 0 B={B} n_in={n_in}")
-    assert_bf16_logits(g[:, 1], o[:, n_in], spread[:, n_in], f"draft step 1 B={B} n_in={n_in}")
+    # the same tokens through the traced verify entry point
+    t = traced_verify(shape, B, n_in + 1, [wl.ctx] * B, seed=3, model_id=synth.DRAFT,
+                      tokens=seq)
+    assert np.array_equal(g[:, 0], t.logits[:, n_in - 1])
+    assert np.array_equal(g[:, 1], t.logits[:, n_in])
+    check_layers(t, [0, 1])
+    check_head(t)
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, None), ("7b", 1, None), ("7b", 8, None),
