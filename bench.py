@@ -94,24 +94,25 @@ def gemm_bytes_per_verify(shape, R):
     """Algorithmic bytes of the weight GEMMs of one forward over R rows: every weight
     once and the activation rows read; outputs: q / K / V / FFN activations in the
     element type (QKV, up), the residual rows read and written in fp32 plus the next
-    normalised product's fp32 input x * g and its per-16-column sums of squares (O-proj,
-    down), fp32 logits (LM head).  A normalised product reads the fp32 x * g rows and
-    their sums of squares when it forms its input itself (R <= 16), else the bf16 rows
-    of the normalise pass."""
+    product's input bf16(x * g) and its per-16-column sums of squares (O-proj, down; the
+    last down writes x * g in fp32 for the normalise pass instead), fp32 logits (LM
+    head).  Normalised products inside the layers also read their rows' sums of
+    squares."""
     d, F, V, L = shape.d_model, shape.d_ffn, shape.vocab, shape.n_layers
     e = shape.elt_bytes()
     ffn_in = 2 * F if shape.ffn_kind == "swiglu" else F
     ss = R * (d // 16) * 4
-    normed_in = R * d * 4 + ss if R <= 16 else R * d * e
-    resid_out = R * d * 4 * 3 + ss
+    resid_out = R * d * 4 * 2 + R * d * e + ss
+    last_out = R * d * 4 * 3 + ss
     # (N, K, input bytes, output bytes) of qkv, O-proj, up, down
-    gemms = [(3 * d, d, normed_in, R * 3 * d * e), (d, d, R * d * e, resid_out),
-             (ffn_in, d, normed_in, R * F * e), (d, F, R * F * e, resid_out)]
+    gemms = [(3 * d, d, R * d * e + ss, R * 3 * d * e), (d, d, R * d * e, resid_out),
+             (ffn_in, d, R * d * e + ss, R * F * e), (d, F, R * F * e, resid_out)]
     total, n = 0, 0
     for N, K, a_in, out in gemms:
         total += L * (N * K * e + a_in + out)
         n += L
-    total += V * d * e + normed_in + R * V * 4
+    total += last_out - resid_out
+    total += V * d * e + R * d * e + R * V * 4
     n += 1
     return total, n
 

@@ -97,7 +97,7 @@ struct FwdWS {
   unsigned* counters; // completion counters: [B*H] attention + 1 GEMM
   int n_counters;
   float* x;           // residual stream [R, d] fp32
-  float* xg;          // bf16: x * g of the next normalised product (act32_index order)
+  float* xg;          // bf16: x * g_f after the last layer (act32_index order)
   void* h;            // normed activations [R, d]
   void* a;            // FFN activations [R, F]
   float* y;           // fp32 models: GEMM outputs [R, max(3d, 2F)]
@@ -272,15 +272,12 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
   return SPEC_OK;
 }
 
-// bf16 models: 5 kernels per layer (up to 3 more with several row tiles).
-//   QKV GEMM (normalised input, RoPE, q out, K/V append) -> attention (+ split merge) ->
-//   O GEMM (x += y, next input x * g2 and its sums of squares) -> up GEMM (normalised
-//   input, SwiGLU / GELU) -> down GEMM (x += y, next input and sums of squares for the
-//   next layer's QKV or the LM head).
-// A normalised product takes bf16(RMSNorm(x) * g): with one row tile (R <= 16) the GEMM
-// forms it from the fp32 x * g rows and the partial sums; with more rows a normalise
-// pass writes it first (the same arithmetic, so a row's product does not depend on the
-// number of rows in the call).
+// bf16 models: 5 kernels per layer.
+//   QKV GEMM (row factor, RoPE, q out, K/V append) -> attention (+ split merge) ->
+//   O GEMM (x += y, next input bf16(x * g2) and its sums of squares) ->
+//   up GEMM (row factor, SwiGLU / GELU) -> down GEMM (x += y, next input and sums of
+//   squares for the next layer's QKV; after the last layer x * g_f in fp32) ->
+//   after the layers: normalise pass (bf16(RMSNorm(x) * g_f)) -> LM head GEMM.
 spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
                          const FwdWS& w, hipStream_t s, const Trace* trace) {
   const spec_model_cfg& c = m->cfg;
@@ -288,7 +285,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
-  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.xg, w.ss,
+  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.h, w.ss,
                                 kv->rope, w.pos0, M, hd, kv->max_len, w.rope_rows, s));
   SPEC_TRACE(0);
   GemmArgs base{};
@@ -305,33 +302,23 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
   base.ss_np = d / 16;
   base.eps = c.norm_eps;
-  const bool fused_norm = R <= 16;
-  // the input of a normalised product over the current x * g rows
-  auto norm_input = [&](GemmArgs& g) -> spec_status {
-    g.K = d;
-    g.lda = d;
-    if (fused_norm) {
-      g.A32 = w.xg;
-      g.ss_in = w.ss;
-    } else {
-      SPEC_LAUNCH(launch_norm_pack(w.xg, w.ss, R, d, c.norm_eps, (uint16_t*)w.h, s));
-      g.A = (const uint16_t*)w.h;
-    }
-    return SPEC_OK;
-  };
   for (int l = 0; l < c.n_layers; ++l) {
     const spec_model::Layer& L = m->layers[l];
+    const bool last = l + 1 == c.n_layers;
     uint16_t* kl = (uint16_t*)((char*)kv->data + (size_t)l * kv->layer_stride * e);
     uint16_t* vl = kl + kv->kv_stride;
     {
       GemmArgs g = base;
       g.mode = EPI_QKV_ROPE;
-      if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
+      g.A = (const uint16_t*)w.h;
+      g.lda = d;
       g.W = (const uint16_t*)L.wqkv;
       g.N = g.N1 = 3 * d;
+      g.K = d;
       g.q_out = (uint16_t*)w.q;
       g.kc = kl;
       g.vc = vl;
+      g.ss_in = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
@@ -354,7 +341,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.K = d;
       g.x = w.x;
       g.gain = L.norm2;
-      g.xg_out = w.xg;
+      g.h_out = (uint16_t*)w.h;
       g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
@@ -362,8 +349,11 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
     SPEC_TRACE(2 * l + 1);
     {
       GemmArgs g = base;
-      if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
+      g.A = (const uint16_t*)w.h;
+      g.lda = d;
+      g.K = d;
       g.act_out = (uint16_t*)w.a;
+      g.ss_in = w.ss;
       g.W = (const uint16_t*)L.w_up;
       if (c.ffn_kind == SPEC_FFN_SWIGLU) {
         g.mode = EPI_SWIGLU;
@@ -386,19 +376,25 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       g.N = g.N1 = d;
       g.K = F;
       g.x = w.x;
-      g.gain = l + 1 < c.n_layers ? m->layers[l + 1].norm1 : m->norm_f;
-      g.xg_out = w.xg;
+      g.gain = last ? m->norm_f : m->layers[l + 1].norm1;
+      // the last layer hands x * g_f in fp32 to the normalise pass of the LM head's input
+      g.h_out = last ? nullptr : (uint16_t*)w.h;
+      g.xg_out = last ? w.xg : nullptr;
       g.ss_out = w.ss;
       Ev ev = timed(g_timing.gemm);
       SPEC_LAUNCH(launch_gemm_bf16(g, s, ev.e0, ev.e1));
     }
     SPEC_TRACE(2 * l + 2);
   }
+  // the LM head's input bf16(RMSNorm(x) * g_f), rounded once after the row factor
+  SPEC_LAUNCH(launch_norm_pack(w.xg, w.ss, R, d, c.norm_eps, (uint16_t*)w.h, s));
   GemmArgs g = base;
   g.mode = EPI_STORE;
-  if (norm_input(g) != SPEC_OK) return SPEC_E_HIP;
+  g.A = (const uint16_t*)w.h;
+  g.lda = d;
   g.W = (const uint16_t*)m->head;
   g.N = g.N1 = V;
+  g.K = d;
   g.C = logits;
   g.ldc = V;
   Ev ev = timed(g_timing.gemm);

@@ -34,27 +34,27 @@ struct GemmArgs {
   // SWIGLU / GELU
   uint16_t* act_out;
   const uint16_t* zeros;  // >= 16 zero bytes (device)
-  // Normalised products (QKV_ROPE, SWIGLU, GELU, STORE) take A = bf16(RMSNorm(x) * g)
-  // of their rows.  Either A already holds it (written by launch_norm_pack), or A32 is
-  // set: then A32 holds x * g in fp32 (act32_index order), ss_in [R][ss_np] the partial
-  // sums of x^2 over 16-column groups, and the kernel forms bf16(x * g * s_r) itself with
-  // the row factor s_r = 1 / sqrt(sum_p ss_in[r][p] / K + eps) (one row tile only).
-  const float* A32;
+  // RMS-normalised input (QKV_ROPE, SWIGLU, GELU, STORE): A = bf16(x * g) of the rows and
+  // ss_in [R][ss_np] the partial sums of x^2 over 16-column groups; the product row r is
+  // scaled by 1 / sqrt(sum_p ss_in[r][p] / K + eps).  NULL: no scaling.
   const float* ss_in;
   int ss_np;
   float eps;
-  // RESID: x [R, N] += Y; xg_out = x * gain in fp32 (act32_index order: the next
-  // normalised product's input) and ss_out [R][N/16] its partial sums of squares per
+  int ss_rows;  // rows of ss_in the epilogue stages in LDS at once (set by the launcher)
+  // RESID: x [R, N] += Y; h_out [R, N] = bf16(x * gain) (the next normalised product's
+  // input) or, when h_out is NULL, xg_out = x * gain in fp32 (act32_index order: the
+  // input of launch_norm_pack), and ss_out [R][N/16] the partial sums of squares per
   // 16-column tile
   float* x;
   const float* gain;
+  uint16_t* h_out;
   float* xg_out;
   float* ss_out;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // h = bf16(xg * s_r) in the packed bf16 order for R rows of width K (xg in act32_index
-// order, s_r from the partial sums ss [R][K/16] exactly as the fused product forms it).
+// order, s_r = 1 / sqrt(sum of the partial sums ss [R][K/16] / K + eps)).
 hipError_t launch_norm_pack(const float* xg, const float* ss, int R, int K, float eps,
                             uint16_t* h, hipStream_t s);
 enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };

@@ -27,16 +27,16 @@
 //   SWIGLU     columns paired (gate n, up n): a = bf16(silu(g) * u)
 //   GELU       a = bf16(gelu(y)), erf form
 //   RESID      x += Y on the residual stream (each column belongs to one tile, so the
-//              update is race-free), xg = x * g in fp32 for the next normalised product
-//              and the tile's partial sums of x^2 per row (16 columns each, summed in
-//              fp64, stored as fp32)
-// A normalised product (QKV_ROPE, SWIGLU, GELU, STORE) multiplies bf16(RMSNorm(x) * g) =
-// bf16(x * g * s) with s = 1 / sqrt(mean(x^2) + eps) summed from those partials in a fixed
-// order: the row factor is applied before the one bf16 rounding of the product's input.
-// With one row tile the product forms that input itself from the fp32 x * g rows (the
-// epilogue wave computes the row factors while the first weights are in flight);
-// larger launches take it from a normalise pass (launch_norm_pack) that does the same
-// arithmetic.
+//              update is race-free), h = bf16(x * g) for the next normalised product and
+//              the tile's partial sums of x^2 per row (16 columns each, summed in fp64,
+//              stored as fp32); before the final norm x * g is written in fp32 instead
+//              (xg_out), for the exact normalise pass of the LM head's input
+// A normalised product inside the layers (QKV_ROPE, SWIGLU, GELU) takes A = bf16(x * g)
+// and scales output row r by s_r = 1 / sqrt(mean(x_r^2) + eps), summed from those
+// partials in a fixed order: RMSNorm(x) * g = s * (x * g), with the row factor taken out
+// of the product, so no separate normalisation pass runs between GEMMs (the one bf16
+// rounding of the input falls before the row factor instead of after it).  The LM head
+// takes bf16(RMSNorm(x) * g) from launch_norm_pack, the rounding after the row factor.
 //
 // fp32 path (small fp32 models): separate simple kernels, one wave per output column.
 #include <hip/hip_ext.h>
@@ -154,25 +154,25 @@ hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd,
   return hipGetLastError();
 }
 
-// LDS the epilogue wave stages its inputs in.  With one row tile every input of the
-// epilogue comes from LDS, copied there by direct global-to-LDS loads that the epilogue
-// wave issues first thing, so they are in flight early and need no registers (once the
-// weight stream saturates HBM a load waits several microseconds, and an epilogue
-// waiting for one would hold the streaming waves at the next tile barrier): the rows'
-// partial sums of squares (when the product forms its normalised input), the RoPE
-// factors of the block's rows and, for RESID, the residual values and norm gains of the
-// current tile.  With more row tiles only the RoPE factors of the tile group and the
-// residual inputs are staged.
+// LDS the epilogue wave stages its inputs in.  With one row tile (MT = 1) every input
+// of the epilogue comes from LDS, copied there by direct global-to-LDS loads that the
+// epilogue wave issues first thing, so they are in flight early and need no registers
+// (once the weight stream saturates HBM a load waits several microseconds, and an
+// epilogue waiting for one would hold the streaming waves at the next tile barrier):
+// the row factors' partial sums, the RoPE factors of the block's rows and, for RESID,
+// the residual values and norm gains of the current tile.  With more row tiles only the
+// partial sums are staged (16 rows at a time) and the other inputs are read from global
+// memory.
 constexpr int SS_NP_MAX = 512;     // partial sums per row (d_model <= 8192)
 constexpr int ROPE_HALF_MAX = 64;  // rotation pairs per head (head_dim <= 128)
 
 // Dynamic LDS of the epilogue wave, sized per launch (epi_lds_bytes): the partial sums
-// of squares of the block's rows (normalising product, one row tile), and the inputs of
-// the tile group being finished: RoPE factors (QKV_ROPE; with one row tile those of every
-// row, else the group's 8 pairs per tile) or residual values and gains (RESID).
-// Everything is requested ahead of use by direct global-to-LDS loads.
+// of squares of the block's rows (all of them, or 16 at a time when they do not fit),
+// and the inputs of the tile group being finished: RoPE factors (QKV_ROPE; with one row
+// tile those of every row, else the group's 8 pairs per tile) or residual values and
+// gains (RESID).  Everything is requested ahead of use by direct global-to-LDS loads.
 struct EpiLds {
-  float* ss;       // [rows][np]
+  float* ss;       // [ss rows][np]
   double2* rope;   // MT == 1: [rows][hd/2]; MT > 1: [NT][MT*16][8]
   float* xres;     // [NT][MT*16][16]
   float* gain;     // [NT][16]
@@ -180,9 +180,9 @@ struct EpiLds {
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline int epi_lds_bytes(int mt, int nt, int mode, int np, int half, int rows,
-                                             bool norm_in) {
-  int b = norm_in ? align16(rows * np * 4) : 0;
+__host__ __device__ inline int epi_lds_bytes(int mt, int nt, int mode, int ss_rows, int np,
+                                             int half, int rows, bool norm_in) {
+  int b = norm_in ? align16(ss_rows * np * 4) : 0;
   if (mode == EPI_QKV_ROPE) b += mt == 1 ? align16(rows * half * 16) : nt * mt * 16 * 8 * 16;
   if (mode == EPI_RESID) b += nt * (mt * 16 * 16 * 4 + 16 * 4);
   return b;
@@ -285,12 +285,13 @@ __device__ __forceinline__ floatx4 sum_partials(const floatx4 (*part)[MT][64], i
 template <int MT>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int r0,
                                                    const floatx4 (*part)[MT][64],
-                                                   const int2* rowinfo, const EpiLds& L,
-                                                   int lane) {
+                                                   const int2* rowinfo, const double* rowscale,
+                                                   const EpiLds& L, int lane) {
   const int nl = lane & 15, gq = lane >> 4, R = g.R, mode = g.mode;
   const bool is_hi = nl >= 8;
   if (mode == EPI_RESID) {
-    // residual update, next input x * g (fp32) and the tile's sums of squares per row
+    // residual update, next input bf16(x * g) (or x * g in fp32) and the tile's sums of
+    // squares per row
     const int col = 16 * t + nl, np = g.N >> 4;
     const float gc = L.gain[nl];
 #pragma unroll 1
@@ -305,7 +306,10 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
           const float xo = L.xres[rr * 16 + nl];
           xn = xo + v[e];
           g.x[(size_t)r * g.N + col] = xn;
-          g.xg_out[act32_index(r, col, g.N)] = xn * gc;
+          if (g.h_out)
+            g.h_out[act_index(r, col, g.N)] = f32_to_bf16(xn * gc);
+          else
+            g.xg_out[act32_index(r, col, g.N)] = xn * gc;
         }
         sq[e] = (double)xn * xn;
       }
@@ -324,9 +328,14 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
     }
     return;
   }
+  // normalised products: the row factor first
 #pragma unroll 1
   for (int mt = 0; mt < MT; ++mt) {
-    const floatx4 v = sum_partials<MT>(part, mt, lane);
+    floatx4 v = sum_partials<MT>(part, mt, lane);
+    if (g.ss_in) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (float)((double)v[e] * rowscale[mt * 16 + 4 * gq + e]);
+    }
     if (mode == EPI_QKV_ROPE) {
       const QkvTile qt = qkv_tile(t, g.d, g.hd);
       const int half = g.hd >> 1, i = qt.i0 + (nl & 7), ii = is_hi ? i + half : i;
@@ -413,18 +422,10 @@ __device__ __forceinline__ void epi_barrier() {
 // for NT tiles at once, which divides the A reads per weight byte (with three or four
 // row tiles the A reads through L1, not HBM, bound the kernel).  Every output element
 // still accumulates its K steps in the same order as with NT = 1.
-// NA (one row tile): the product forms its normalised input itself.  A is then the fp32
-// rows x * g (act32_index order, two 16-byte loads per lane and slice instead of one);
-// the epilogue wave computes the row factors from the staged partial sums while the
-// first steps are in flight and publishes them at one extra barrier, and each
-// streaming wave multiplies its A fragments by its row's factor and rounds them to bf16
-// right before the MFMAs -- the same arithmetic as launch_norm_pack, so a row's product
-// is bitwise the same on either path.
-template <int MT, int NT, bool NA>
+template <int MT, int NT>
 __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   constexpr int P = SPEC_GEMM_RING;
   static_assert(MT > 1 || NT == 1, "one row tile uses single column tiles");
-  static_assert(!NA || (MT == 1 && NT == 1), "the fused normalisation takes one row tile");
   __shared__ floatx4 part[2][NT][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
   __shared__ double rowscale[MT * 16];
@@ -438,10 +439,11 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     const int rows = min(MT * 16, g.R - r0);  // >= 1
     const int np = g.ss_np, half = g.hd >> 1;
     EpiLds L;
+    const int ss_rows = min(g.ss_rows, g.R);  // partial-sum rows the LDS holds at once
     {
       char* p = reinterpret_cast<char*>(epi_dyn);
       L.ss = reinterpret_cast<float*>(p);
-      if (NA) p += align16(rows * np * 4);
+      if (g.ss_in) p += align16(ss_rows * np * 4);
       L.rope = reinterpret_cast<double2*>(p);
       if (g.mode == EPI_QKV_ROPE) p += MT == 1 ? align16(g.R * half * 16) : NT * MT * 16 * 8 * 16;
       L.xres = reinterpret_cast<float*>(p);
@@ -468,7 +470,9 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
       ntok[k] = g.ntok_eff ? g.ntok_eff[b] : g.M;
       p0v[k] = g.pos0 ? g.pos0[b] : 0;
     }
-    if (NA) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, rows * np * 4, lane);
+    const bool ss_all = ss_rows >= rows;
+    if (g.ss_in)
+      lds_copy(g.ss_in + (size_t)r0 * np, L.ss, (ss_all ? rows : min(16, rows)) * np * 4, lane);
     if (MT == 1 && g.mode == EPI_QKV_ROPE)
       lds_copy(g.rope_rows + (size_t)r0 * half * 2, L.rope, rows * half * 16, lane);
     stage_group(bx);
@@ -491,10 +495,17 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
       if (rr < MT * 16) rowinfo[rr] = info;
     }
     wait_vm();
-    if constexpr (NA) {
-      // the row factors, published to the streaming waves at their first barrier
-      row_factors(L.ss, rows, np, g.K, g.eps, lane, rowscale);
-      epi_barrier();
+    if (g.ss_in) {
+      for (int rb = 0; rb < MT && 16 * rb < rows; ++rb) {
+        const float* src = L.ss + (ss_all ? rb * 16 * np : 0);
+        if (!ss_all && rb > 0) {  // 16 rows at a time: the next batch (requested late)
+          wave_lds_sync();
+          lds_copy(g.ss_in + (size_t)(r0 + 16 * rb) * np, L.ss, min(16, rows - 16 * rb) * np * 4,
+                   lane);
+          wait_vm();
+        }
+        row_factors(src, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
+      }
     }
     wave_lds_sync();
     for (int ct = 0; ct < nt; ++ct) {
@@ -505,8 +516,8 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
         if (MT > 1) Ln.rope = L.rope + n * MT * 16 * 8;
         Ln.xres = L.xres + n * MT * 16 * 16;
         Ln.gain = L.gain + n * 16;
-        gemm_tile_epilogue<MT>(g, (bx + ct * G) * NT + n, r0, part[ct & 1][n], rowinfo, Ln,
-                               lane);
+        gemm_tile_epilogue<MT>(g, (bx + ct * G) * NT + n, r0, part[ct & 1][n], rowinfo, rowscale,
+                               Ln, lane);
       }
       if (ct + 1 < nt && (g.mode == EPI_RESID || (MT > 1 && g.mode == EPI_QKV_ROPE))) {
         wave_lds_sync();  // this group's slots are read
@@ -527,7 +538,6 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   const int last_step = wact ? (nsuper - 1 - wv) / GW : 0;
   const size_t tile_elems = (size_t)nsuper * 2048;  // one packed tile
   const u16* arow[MT];
-  const float* arow32 = nullptr;
   bool aok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -537,9 +547,6 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     // arow[mt] + js * 2048 + s * 512
     arow[mt] = g.A + (size_t)(blockIdx.y * MT + mt) * (size_t)nsuper * 2048 + 8 * (4 * nl + gq);
   }
-  // NA: the fp32 rows (act32_index): this lane's 16 bytes of step js, slice s, half h at
-  // arow32 + js * 2048 + (2 s + h) * 256
-  if (NA) arow32 = g.A32 + 4 * (4 * nl + gq);
   floatx4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -547,13 +554,9 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     for (int n = 0; n < NT; ++n) acc[mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int Q = P + 1;  // register buffers: P steps in flight while one is multiplied
-  constexpr int QA = NA ? 1 : Q;
-  constexpr int QF = NA ? Q : 1;
   bf16x8 wf[Q][NT][4];
-  bf16x8 af[QA][MT][4];
-  float4v af32[QF][4][2];
+  bf16x8 af[Q][MT][4];
   const u16* zblk = g.zeros;
-  float sv = 0.f;  // NA: this lane's row factor (0 on padding rows)
   // issue stream: tile iteration it, step is; a step past the wave's last one in a tile,
   // or past the workgroup's last tile, re-reads an in-bounds W segment (cache hit) and
   // pairs it with zero A fragments, so every wave runs the same branch-free schedule.
@@ -567,23 +570,12 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         wf[slot][n][s] = ld8_nt(wp + n * tile_elems + js * 2048 + 512 * s, true);
-    if constexpr (NA) {
-      const bool ok = valid && aok[0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          af32[slot][s][h] = *reinterpret_cast<const float4v*>(
-              ok ? arow32 + (size_t)js * 2048 + (2 * s + h) * 256
-                 : reinterpret_cast<const float*>(zblk));
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          af[slot][mt][s] = ld8((valid && aok[mt]) ? arow[mt] + (size_t)js * 2048 + 512 * s : zblk,
-                                true);
-    }
+        af[slot][mt][s] = ld8((valid && aok[mt]) ? arow[mt] + (size_t)js * 2048 + 512 * s : zblk,
+                              true);
     if (++is == S) {
       is = 0;
       ++it;
@@ -592,30 +584,14 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   };
   int ct = 0, cs = 0;  // consume stream: tile iteration, step
   auto consume = [&](int slot) {
-    if constexpr (NA) {
-      // bf16(x * g * s): the fp32 product rounded once, as launch_norm_pack rounds it
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-        u16x8 a;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = f32_to_bf16(af32[slot][s][0][e] * sv);
-          a[4 + e] = f32_to_bf16(af32[slot][s][1][e] * sv);
-        }
-        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                            wf[slot][0][s], acc[0][0], 0, 0, 0);
-      }
-    } else {
+      for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mt][s], wf[slot][n][s],
-                                                                 acc[mt][n], 0, 0, 0);
-    }
+        for (int s = 0; s < 4; ++s)
+          acc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mt][s], wf[slot][n][s],
+                                                               acc[mt][n], 0, 0, 0);
     if (++cs == S) {
       cs = 0;
       if (ct < nt) {
@@ -636,8 +612,6 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
   // multiplied last) and then multiplies its own buffer, so the requests never wait
   // behind the MFMA chain.  The last round's requests read in-bounds W past the end
   // (cache hits, never multiplied), so the loop body is the only copy of the tile code.
-  // NA: the first step waits, after its requests are out, for the row factors (the
-  // epilogue wave's first barrier).
   const int F = nt * S;  // steps of this wave
   const int T = (F + Q - 1) / Q;
 #pragma unroll
@@ -647,13 +621,6 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16(GemmArgs g) {
     for (int u = 0; u < Q; ++u) {
       issue((u + P) % Q);
       __builtin_amdgcn_sched_barrier(0);
-      if (NA && u == 0 && t == 0) {
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __asm__ volatile("" ::: "memory");
-        sv = aok[0] ? (float)rowscale[nl] : 0.f;
-        __builtin_amdgcn_sched_barrier(0);
-      }
       consume(u);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -684,15 +651,18 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
   constexpr int PT = TPW > 4 ? TPW : 4;
   __shared__ floatx4 part[PT][GW][MT][64];
   __shared__ int2 rowinfo[MT * 16];
+  __shared__ double rowscale[MT * 16];
   extern __shared__ float4 epi_dyn[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bx = blockIdx.x, G = gridDim.x;
   const int r0 = blockIdx.y * (MT * 16);
   const int rows = min(MT * 16, g.R - r0);  // >= 1
+  const int np = g.ss_np;
   EpiLds L;
   {
     char* p = reinterpret_cast<char*>(epi_dyn);
-    L.ss = nullptr;
+    L.ss = reinterpret_cast<float*>(p);
+    if (g.ss_in) p += align16(16 * np * 4);
     L.rope = reinterpret_cast<double2*>(p);
     if (g.mode == EPI_QKV_ROPE) p += TPW * MT * 16 * 8 * 16;
     L.xres = reinterpret_cast<float*>(p);
@@ -720,8 +690,8 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
   for (int c = 0; c < nchunks; ++c) {
     if (wv == GW) {
       if (c == 0) {
-        // requests first: counts and start positions and the chunk's epilogue inputs;
-        // then the streaming waves start
+        // requests first: counts and start positions, the first 16 rows' sums of squares,
+        // the chunk's epilogue inputs; then the streaming waves start
         int ntok[(MT * 16 + 63) / 64], p0v[(MT * 16 + 63) / 64];
 #pragma unroll
         for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
@@ -729,6 +699,7 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
           ntok[k] = g.ntok_eff ? g.ntok_eff[b] : g.M;
           p0v[k] = g.pos0 ? g.pos0[b] : 0;
         }
+        if (g.ss_in) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, min(16, rows) * np * 4, lane);
         stage_chunk(0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
@@ -744,6 +715,19 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
           if (rr < MT * 16) rowinfo[rr] = info;
         }
         wait_vm();
+        if (g.ss_in) {
+          // later 16-row batches are requested behind the weight stream; the results are
+          // needed only at the end of the chunk
+          for (int rb = 0; rb < MT && 16 * rb < rows; ++rb) {
+            if (rb > 0) {
+              wave_lds_sync();
+              lds_copy(g.ss_in + (size_t)(r0 + 16 * rb) * np, L.ss,
+                       min(16, rows - 16 * rb) * np * 4, lane);
+              wait_vm();
+            }
+            row_factors(L.ss, min(16, rows - 16 * rb), np, g.K, g.eps, lane, rowscale + 16 * rb);
+          }
+        }
       } else {
         stage_chunk(c);
         wait_vm();
@@ -861,14 +845,14 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
       Lj.rope = L.rope + j * MT * 16 * 8;
       Lj.xres = L.xres + j * MT * 16 * 16;
       Lj.gain = L.gain + j * 16;
-      gemm_tile_epilogue<MT>(g, t, r0, part[j], rowinfo, Lj, lane);
+      gemm_tile_epilogue<MT>(g, t, r0, part[j], rowinfo, rowscale, Lj, lane);
     }
     __syncthreads();  // the chunk's partials and input slots may be reused
   }
 }
 
-__host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode) {
-  int b = 0;
+__host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode, int np, bool norm_in) {
+  int b = norm_in ? align16(16 * np * 4) : 0;
   if (mode == EPI_QKV_ROPE) b += tpw * mt * 16 * 8 * 16;
   if (mode == EPI_RESID) b += tpw * (mt * 16 * 16 * 4 + 16 * 4);
   return b;
@@ -876,11 +860,10 @@ __host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode) {
 
 // ------------------------------------------------------------------ normalise pass --
 
-// h = bf16(xg * s_r) for the rows of a normalised product that the one-row-tile kernel
-// does not take (several row tiles): one 256-thread workgroup per row; the first wave
-// forms the row factor from the staged partial sums with row_factors (the same order and
-// arithmetic as the fused product), then every thread rounds 8-column groups into the
-// packed bf16 order.
+// h = bf16(xg * s_r): the LM head's input, RMSNorm(x) * g rounded once after the row
+// factor.  One 256-thread workgroup per row; the first wave forms the row factor from the
+// staged partial sums with row_factors (the order the products inside the layers use),
+// then every thread rounds 8-column groups into the packed bf16 order.
 __global__ __launch_bounds__(256) void k_norm_pack(const float* __restrict__ xg,
                                                    const float* __restrict__ ss, int K, float eps,
                                                    u16* __restrict__ h) {
@@ -1013,22 +996,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   const int ngroups = g.ntiles / NTc;
   const int per = cdiv(ngroups, gmax);
   const int G = cdiv(ngroups, per);
-  if (g.A32) {
-    // the product forms its normalised input: one row tile, the rows' partial sums given
-    if (tiles != 1 || !g.ss_in || g.ss_np != g.K / 16 || g.ss_np > SS_NP_MAX || g.ss_np % 8)
-      return hipErrorInvalidValue;
-  } else if (g.ss_in) {
-    return hipErrorInvalidValue;  // a bf16 A is used as given
-  }
+  if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
-  if (g.A32) {
-    const unsigned lds =
-        (unsigned)epi_lds_bytes(1, 1, g.mode, g.ss_np, g.hd / 2, g.R, true);
-    if (2 * GW * 1024 + 16 * (8 + 8) + (int)lds > 160 * 1024) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((k_gemm_bf16<1, 1, true>), dim3(G, 1), dim3(GT), lds, s, e0, e1, 0, g);
-    return hipGetLastError();
-  }
   {
     // several row tiles and several tiles per workgroup: the K-outer kernel, in chunks
     // of equal size, at most ko_tpw_max tiles and as many as its LDS allows
@@ -1038,8 +1008,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
       for (int tcap = tmax; tcap >= 2; --tcap) {
         const int tpw = cdiv(kper, cdiv(kper, tcap));
         const int kG = cdiv(g.ntiles, kper);
-        const int kstatic = std::max(tpw, 4) * GW * mt * 1024 + mt * 16 * 8;
-        const int kdyn = ko_lds_bytes(mt, tpw, g.mode);
+        const int kstatic = std::max(tpw, 4) * GW * mt * 1024 + mt * 16 * (8 + 8);
+        const int kdyn = ko_lds_bytes(mt, tpw, g.mode, g.ss_np, g.ss_in != nullptr);
         if (kstatic + kdyn > 160 * 1024) continue;
         const dim3 grid(kG, rowblocks);
         if (mt == 2) launch_ko<2>(tpw, grid, (unsigned)kdyn, s, e0, e1, g, kper);
@@ -1049,13 +1019,18 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
       }
     }
   }
+  // stage every row's partial sums of squares at once when the LDS holds them next to
+  // the tile partials (static LDS of the kernel), else 16 rows at a time
   const int static_lds = 2 * NTc * GW * mt * 1024 + mt * 16 * (8 + 8);
-  const unsigned lds =
-      (unsigned)epi_lds_bytes(mt, NTc, g.mode, g.ss_np, g.hd / 2, g.R, false);
+  g.ss_rows = mt * 16;
+  if (static_lds + epi_lds_bytes(mt, NTc, g.mode, std::min(g.ss_rows, g.R), g.ss_np, g.hd / 2,
+                                 g.R, g.ss_in != nullptr) > 160 * 1024)
+    g.ss_rows = 16;
+  const unsigned lds = (unsigned)epi_lds_bytes(mt, NTc, g.mode, std::min(g.ss_rows, g.R),
+                                               g.ss_np, g.hd / 2, g.R, g.ss_in != nullptr);
   if (static_lds + (int)lds > 160 * 1024) return hipErrorInvalidValue;
 #define SPEC_GEMM_LAUNCH(MT_, NT_, GY)                                                     \
-  hipExtLaunchKernelGGL((k_gemm_bf16<MT_, NT_, false>), dim3(G, GY), dim3(GT), lds, s, e0, e1, \
-                        0, g)
+  hipExtLaunchKernelGGL(k_gemm_bf16<MT_, NT_>, dim3(G, GY), dim3(GT), lds, s, e0, e1, 0, g)
   if (tiles <= 1) {
     SPEC_GEMM_LAUNCH(1, 1, 1);
   } else if (tiles <= 2) {

@@ -53,7 +53,7 @@ struct SamplingKnobs {
 namespace specdec {
 
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float* x, float* xg, float* ss, const double* rope,
+                             const float* g, float* x, void* h, float* ss, const double* rope,
                              const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
                              hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,

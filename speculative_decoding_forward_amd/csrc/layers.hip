@@ -78,14 +78,14 @@ __global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok
 }
 
 // bf16 models: x[r, :] = E[tok[r], :] (fp32), the first layer's normalised-product input
-// xg = x * g (fp32, act32_index order) and the partial sums of x^2 over each 16-column
-// group (summed in fp64, stored as fp32: ss[r][c], in column order), from which the QKV
-// product forms bf16(RMSNorm(x) * g); also the row's RoPE factors for all layers.  One
-// block (256 threads) per row; a thread takes one 16-column group at a time (two 16-byte
-// loads; d is a multiple of 128).
+// h = bf16(x * g) and the partial sums of x^2 over each 16-column group (summed in
+// fp64, stored as fp32: ss[r][c], in column order), from which the QKV product takes its row factor
+// 1 / sqrt(mean(x^2) + eps); also the row's RoPE factors for all layers.  One block (256
+// threads) per row; a thread takes one 16-column group at a time (two 16-byte loads; d is
+// a multiple of 128).
 __global__ __launch_bounds__(256) void k_embed_norm(
     const u16* __restrict__ E, const int32_t* __restrict__ tok, int d, const float* __restrict__ g,
-    float* __restrict__ x, float* __restrict__ xg, float* __restrict__ ss,
+    float* __restrict__ x, u16* __restrict__ h, float* __restrict__ ss,
     const double* __restrict__ rope, const int32_t* __restrict__ pos0, int M, int hd, int max_len,
     double* __restrict__ rope_rows) {
   const int r = blockIdx.x;
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(
   const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)tok[r] * d);
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
   const float4* gr = reinterpret_cast<const float4*>(g);
+  // h in the packed activation order (act_layout.h): 8 consecutive columns stay contiguous
   const int np = d / 16;
   for (int c = threadIdx.x; c < np; c += 256) {
     double sq = 0.0;
@@ -119,11 +120,13 @@ __global__ __launch_bounds__(256) void k_embed_norm(
       xr[2 * c8] = float4{v[0], v[1], v[2], v[3]};
       xr[2 * c8 + 1] = float4{v[4], v[5], v[6], v[7]};
       const float4 g0 = gr[2 * c8], g1 = gr[2 * c8 + 1];
-      // x * g: columns 8 c8 .. + 4 and + 4 .. + 8 are two contiguous float4 of the order
-      *reinterpret_cast<float4*>(xg + act32_index(r, 8 * c8, d)) =
-          float4{v[0] * g0.x, v[1] * g0.y, v[2] * g0.z, v[3] * g0.w};
-      *reinterpret_cast<float4*>(xg + act32_index(r, 8 * c8 + 4, d)) =
-          float4{v[4] * g1.x, v[5] * g1.y, v[6] * g1.z, v[7] * g1.w};
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = f32_to_bf16(v[2 * k] * gg[2 * k]) |
+               ((uint32_t)f32_to_bf16(v[2 * k + 1] * gg[2 * k + 1]) << 16);
+      *reinterpret_cast<uint4*>(h + act_index(r, 8 * c8, d)) = uint4{o[0], o[1], o[2], o[3]};
 #pragma unroll
       for (int k = 0; k < 8; ++k) sq += (double)v[k] * v[k];
     }
@@ -330,10 +333,10 @@ hipError_t launch_attention_f32(const float* q, const float* kcache, const float
 
 
 hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float* x, float* xg, float* ss, const double* rope,
+                             const float* g, float* x, void* h, float* ss, const double* rope,
                              const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
                              hipStream_t s) {
-  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, x, xg, ss, rope, pos0, M,
+  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, x, (u16*)h, ss, rope, pos0, M,
                                  hd, max_len, rope_rows);
   return hipGetLastError();
 }
