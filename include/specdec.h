@@ -291,6 +291,22 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
                                  int32_t* n_pending, void* const* debug, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* spec_accept_resample for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results without debug exports or workspace.  Its scratch is a 64 KB
+ * device array inside the library (each GPU holds its own copy until the process ends),
+ * so spec_accept_workspace_bytes(B, K) must not exceed 65536 (else SPEC_E_CAPACITY; e.g.
+ * B <= 256 at K <= 16).  Calls that overlap on one GPU (concurrent streams) share that
+ * array and race: issue them on one stream.  The first call on a device looks up the
+ * array's device address (SPEC_E_HIP if that fails). */
+spec_status spec_accept_resample_static(const float* p_logits, const float* q_logits,
+                                        const int32_t* x_tilde, int B, int K, int V,
+                                        const spec_sampling* knobs, uint64_t seed,
+                                        uint64_t round, uint64_t* round_dev, int32_t* out_tok,
+                                        int32_t* n_out, int32_t* row_status, spec_kv* tkv,
+                                        spec_kv* dkv, int32_t* pending, int32_t* n_pending,
+                                        void* stream);
+
 /* ------------------------------------------------------------------ measurement --- */
 
 /* Kernel timing for measurement.  While enabled, HIP events are recorded on the launch

@@ -25,7 +25,8 @@ SYMBOLS = [
     "spec_kv_create", "spec_kv_destroy", "spec_kv_data", "spec_kv_import", "spec_kv_export",
     "spec_kv_rollback",
     "spec_workspace_bytes", "spec_verify_forward", "spec_verify_forward_trace", "spec_draft_step",
-    "spec_accept_workspace_bytes", "spec_accept_resample", "spec_verify_tokens",
+    "spec_accept_workspace_bytes", "spec_accept_resample", "spec_accept_resample_static",
+    "spec_verify_tokens",
     "spec_status_str", "spec_last_hip_error", "spec_abi_version", "spec_timing_enable",
     "spec_timing_read",
 ]
@@ -98,6 +99,8 @@ def load(path=None):
         "spec_verify_tokens": (I32, [P, P, P, I32, I32, P, P]),
         "spec_accept_resample": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P, P, P,
                                        P, P, ctypes.POINTER(P), P, SZ, P]),
+        "spec_accept_resample_static": (I32, [P, P, P, I32, I32, I32, smp, U64, U64, P, P, P, P,
+                                              P, P, P, P, P]),
         "spec_status_str": (ctypes.c_char_p, [I32]),
         "spec_last_hip_error": (I32, []),
         "spec_abi_version": (I32, []),

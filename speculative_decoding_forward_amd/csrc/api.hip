@@ -796,6 +796,61 @@ spec_status spec_accept_resample(const float* p_logits, const float* q_logits,
   return SPEC_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of spec_accept_resample_static: a file-scope device array (each GPU the library
+// runs on holds its own copy until the process ends).  In host code `scratch` only names
+// the symbol; its device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+constexpr size_t kStaticScratchBytes = 64 * 1024;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// This device's address of `scratch`, resolved on first use; nullptr on failure.
+void* static_scratch(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status spec_accept_resample_static(const float* p_logits, const float* q_logits,
+                                        const int32_t* x_tilde, int B, int K, int V,
+                                        const spec_sampling* knobs, uint64_t seed,
+                                        uint64_t round, uint64_t* round_dev, int32_t* out_tok,
+                                        int32_t* n_out, int32_t* row_status, spec_kv* tkv,
+                                        spec_kv* dkv, int32_t* pending, int32_t* n_pending,
+                                        void* stream) {
+  if (B < 1 || K < 1) return SPEC_E_INVALID;
+  if (spec_accept_workspace_bytes(B, K) > kStaticScratchBytes) return SPEC_E_CAPACITY;
+  hipError_t err = hipSuccess;
+  void* ws = static_scratch(&err);
+  if (!ws) return hip_fail(err);
+  // every slot the kernels read is written earlier in the same call: nothing to clear
+  return spec_accept_resample(p_logits, q_logits, x_tilde, B, K, V, knobs, seed, round,
+                              round_dev, out_tok, n_out, row_status, tkv, dkv, pending,
+                              n_pending, nullptr, ws, kStaticScratchBytes, stream);
+}
+
 spec_status spec_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   g_timing.on = on != 0;
