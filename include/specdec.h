@@ -225,6 +225,10 @@ spec_status spec_verify_forward_trace(const spec_model* m, spec_kv* kv, const in
  * in {1,2}: the draft's pending tokens); step s > 0 takes x_tilde[b, s-1].
  *   x_tilde  [B, K] int32, column `step` written
  *   q_logits [B, K, V] fp32, row `step` written (the draft logits at the last input)
+ * row_status [B] int32 or NULL: OR-ed with SPEC_ROW_KV_OVERFLOW / SPEC_ROW_BAD_TOKEN as in
+ * spec_verify_forward, and with SPEC_ROW_NONFINITE when the step's draft logits are not
+ * all finite (x~_step is then the placeholder 0; the accept step emits nothing for the
+ * row).
  * A step-0 call records the row's pre-round cache length for spec_accept_resample.
  * round_dev (device, NULL = use `round`): when set, the round number is read from
  * *round_dev at execution time, so a captured HIP graph of a whole round can be

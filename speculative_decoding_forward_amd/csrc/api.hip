@@ -738,7 +738,7 @@ spec_status spec_draft_step(const spec_model* draft, spec_kv* dkv, const int32_t
   if (st != SPEC_OK) return st;
   SPEC_LAUNCH(launch_draft_sample(w.logits, B, M, w.ntok2, step, K, draft->cfg.vocab,
                                   to_knobs(knobs), seed, round, round_dev, x_tilde, q_logits,
-                                  s));
+                                  row_status, s));
   return SPEC_OK;
 }
 

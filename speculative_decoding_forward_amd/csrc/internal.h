@@ -120,7 +120,7 @@ hipError_t launch_select(const int32_t* x_tilde, int B, int K, const int32_t* re
 hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t* n_in,
                                int step, int K, int V, SamplingKnobs kn, uint64_t seed,
                                uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
-                               float* q_logits, hipStream_t s);
+                               float* q_logits, int32_t* row_status, hipStream_t s);
 hipError_t launch_rollback(int32_t* len, const int32_t* new_len, int B, hipStream_t s);
 hipError_t launch_rope_table(double* tab, int max_len, int hd, double theta, hipStream_t s);
 // R rows of width K of an activation buffer (bf16: the packed order; fp32: natural) into

@@ -582,13 +582,16 @@ __global__ void k_select(const int32_t* __restrict__ x_tilde, int B, int K,
 }
 
 // Draft step sampler: one workgroup per row b.  Copies the logits of the row's last
-// input position into q_logits[b, step], processes them and draws x~_step.
+// input position into q_logits[b, step], processes them and draws x~_step.  A row whose
+// logits are not all finite gets SPEC_ROW_NONFINITE in row_status (when given) and the
+// placeholder token 0, which keeps the next steps' inputs in range; the accept step
+// then emits nothing for the row (its q row is non-finite too).
 template <int VPT>
 __global__ __launch_bounds__(VT) void k_draft_sample(
     const float* __restrict__ logits, int M, const int32_t* __restrict__ n_in, int step,
     int K, int V, SamplingKnobs kn, uint64_t seed, uint64_t round,
     const uint64_t* __restrict__ round_dev, int32_t* __restrict__ x_tilde,
-    float* __restrict__ q_logits) {
+    float* __restrict__ q_logits, int32_t* __restrict__ row_status) {
   __shared__ VocabLDS sh;
   if (round_dev) round = *round_dev;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -606,6 +609,8 @@ __global__ __launch_bounds__(VT) void k_draft_sample(
     store_w<VPT>(v, V, sh);
     x = inverse_cdf_lds(V, u, sh);
     if (x < 0) x = 0;
+  } else if (tid == 0 && row_status) {
+    row_status[b] |= SPEC_ROW_NONFINITE;
   }
   if (tid == 0) x_tilde[b * K + step] = x;
 }
@@ -664,9 +669,10 @@ hipError_t launch_select(const int32_t* x_tilde, int B, int K, const int32_t* re
 hipError_t launch_draft_sample(const float* logits, int B, int M, const int32_t* n_in,
                                int step, int K, int V, SamplingKnobs kn, uint64_t seed,
                                uint64_t round, const uint64_t* round_dev, int32_t* x_tilde,
-                               float* q_logits, hipStream_t s) {
+                               float* q_logits, int32_t* row_status, hipStream_t s) {
   VPT_DISPATCH(V, (k_draft_sample<P><<<B, VT, 0, s>>>(logits, M, n_in, step, K, V, kn, seed,
-                                                     round, round_dev, x_tilde, q_logits)));
+                                                     round, round_dev, x_tilde, q_logits,
+                                                     row_status)));
   return hipGetLastError();
 }
 

@@ -186,3 +186,64 @@ def test_chi_square_million_rounds_on_gpu():
     expect = theory.expected_tokens_rows(betas)
     print(f"mean n_out {nsum / n:.4f} expected {expect:.4f}")
     assert abs(nsum / n - expect) < 0.01
+
+
+def test_empty_residual_falls_back_to_p():
+    """A rejection whose residual max(0, p - q) is empty ([LENS] §2.3; the reading that
+    such a row samples P_a): q = p row for row, and each row's first draft token lies
+    outside the top-k set, so p(x~) = q(x~) = 0 on both sides and the token is rejected
+    with nothing left in the residual.  The GPU must set SPEC_ROW_RESIDUAL_EMPTY (and
+    Q_ZERO) and emit the oracle's draw from P_0 with the resample uniform."""
+    B, K, V = 6, 3, 4096
+    knobs = (0.9, 16, 1.0)
+    p, _ = synth.vocab_logits(21, B, K, V)
+    q = p[:, :K].copy()
+    xt = np.zeros((B, K), dtype=np.int64)
+    for b in range(B):
+        P0 = sampling.transform(p[b, 0], *knobs)
+        xt[b, 0] = int(np.nonzero(P0 == 0)[0][b])       # outside the kept set
+        xt[b, 1:] = np.argmax(p[b, 1:K], axis=-1)
+    g = gpu_accept(p, q, xt, knobs, seed=13, rnd=2)
+    for b in range(B):
+        P = np.stack([sampling.transform(r, *knobs) for r in p[b]])
+        Q = np.stack([sampling.transform(r, *knobs) for r in q[b]])
+        ua = philox.uniform(13, 2, np.arange(K), b, 1)
+        ur = philox.uniform(13, 2, np.arange(K + 1), b, 2)
+        toks, n, a, st = sampling.accept_resample(P, Q, xt[b], ua, ur)
+        assert a == 0 and st & sampling.ST_RESIDUAL_EMPTY
+        assert g["n_out"][b] == 1 and g["out"][b, 0] == toks[0], (b, g["out"][b], toks)
+        assert g["status"][b] & binding.ROW_RESIDUAL_EMPTY
+        assert g["status"][b] & binding.ROW_Q_ZERO
+        assert g["cand"][b, 0] == toks[0]
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_top_k_ties_are_kept(T):
+    """Ties at the k-th largest logit are all kept on both p and q ([NOTE] Recommendation
+    R3: knobs before the rule; the tie reading): rows with a tie planted across the
+    top-k threshold keep every tied token, exactly as the oracle's transform does."""
+    B, K, V, k = 4, 2, 2048, 10
+    p, q = synth.vocab_logits(31, B, K, V)
+    rng = np.random.default_rng(5)
+    for arr in (p, q):
+        for b in range(arr.shape[0]):
+            for j in range(arr.shape[1]):
+                row = arr[b, j]
+                order = np.argsort(-row)
+                tied = rng.choice(np.arange(8, 40), 6, replace=False)  # straddle rank k
+                row[order[tied]] = row[order[k - 1]]
+    knobs = (T, k, 1.0)
+    xt = draft_tokens(q, knobs, 31, 0)
+    g = gpu_accept(p, q, xt, knobs, seed=17, rnd=1)
+    for b in range(B):
+        for j in range(K + 1):
+            P = sampling.transform(p[b, j], *knobs)
+            assert np.array_equal(g["pp"][b, j] > 0, P > 0), (b, j)
+            assert (P > 0).sum() > k                       # the ties were kept
+            assert np.abs(g["pp"][b, j] - P).max() <= 1e-6
+        for j in range(K):
+            Q = sampling.transform(q[b, j], *knobs)
+            assert np.array_equal(g["qp"][b, j] > 0, Q > 0), (b, j)
+    tally = Tally()
+    check_accept_against_oracle(p, q, xt, knobs, 17, 1, g, tally)
+    assert sum(tally.near.values()) <= 1, tally.report()

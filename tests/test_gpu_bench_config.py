@@ -1,5 +1,6 @@
-"""The round exactly as the bench times it -- 7B shape, batch 1, K=5, context 2048, one
-captured round replayed as a HIP graph -- checked at full size against the oracle's rule.
+"""The round exactly as the bench times it -- 7B shape, batch 1 (and batch 8), K=5,
+context 2048, one captured round replayed as a HIP graph -- checked at full size against
+the oracle's rule.
 
 The oracle cannot run a 32-layer 7B forward here, so the logits are taken from the GPU
 and the oracle re-derives, one row at a time, every decision the round made from them
@@ -66,10 +67,10 @@ def _rule_near(p, q, xt, ua, ur, knobs, a):
     return dist <= 1e-6 * S or _tp_margin(p[a], knobs) <= 1e-6
 
 
-@pytest.mark.parametrize("greedy", [False, True])
-def test_bench_rounds_follow_the_rule_at_full_size(greedy):
+@pytest.mark.parametrize("greedy,B", [(False, 1), (True, 1), (False, 8)])
+def test_bench_rounds_follow_the_rule_at_full_size(greedy, B):
     wl = synth.WORKLOADS["7b"]
-    B, K, seed = wl.batch, wl.K, 0
+    K, seed = wl.K, 0
     knobs = (0.0, 0, 1.0) if greedy else (wl.temperature, wl.top_k, wl.top_p)
     Wt = synth.make_weights(wl.target, seed=seed, model_id=synth.TARGET, device=DEV)
     Wd = synth.make_weights(wl.draft, seed=seed, model_id=synth.DRAFT, device=DEV)

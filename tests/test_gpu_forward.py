@@ -278,3 +278,31 @@ def test_kv_import_export_roundtrip(dtype, hd, max_len):
     got = kv.export(max_len)
     assert torch.equal(got[:, :, :, :, :n], part[:, :, :, :, :n])
     assert torch.equal(got[:, :, :, :, n:], full[:, :, :, :, n:])
+
+
+def test_draft_step_flags_non_finite_rows():
+    """A draft step whose logits are not all finite (a NaN planted in row 1's cache at a
+    valid position) sets SPEC_ROW_NONFINITE for that row only and emits the placeholder
+    token 0 for it; the other row samples as usual."""
+    shape = bf16_micro("swiglu")
+    m, _ = setup(shape, seed=8, model_id=synth.DRAFT)
+    B, max_len, n = 2, 64, 40
+    fill = synth.kv_fill(shape, B, max_len, n, seed=8, device=DEV)
+    fill[0, 1, 1, 0, 5, :] = float("nan")          # layer 0, row 1, V, head 0, position 5
+    kv = binding.KVCache(shape, B, max_len)
+    kv.import_(fill)
+    kv.len.fill_(n)
+    K, V = 2, shape.vocab
+    in_tok = to_dev(np.array([[3, -1], [4, -1]], np.int32))
+    n_in = to_dev(np.array([1, 1], np.int32))
+    x_tilde = torch.full((B, K), -7, dtype=torch.int32, device=DEV)
+    q_logits = torch.zeros((B, K, V), dtype=torch.float32, device=DEV)
+    st = torch.zeros(B, dtype=torch.int32, device=DEV)
+    binding.draft_step(m, kv, in_tok, n_in, 0, (1.0, 0, 1.0), 3, 0, x_tilde, q_logits,
+                       m.workspace(B, 2, max_len), row_status=st)
+    torch.cuda.synchronize()
+    s = st.cpu().numpy()
+    assert s[0] == 0 and s[1] & binding.ROW_NONFINITE
+    xt = x_tilde.cpu().numpy()
+    assert xt[1, 0] == 0 and 0 <= xt[0, 0] < V
+    assert np.all(np.isfinite(q_logits[0, 0].cpu().numpy()))
