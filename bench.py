@@ -14,6 +14,7 @@ roofline object covers the dominant kernel (the weight-streaming GEMM), timed li
 HIP events on its launch stream over the timed rounds.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
     ap.add_argument("--sweep-K", default="1,2,3,4,5,6,7,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-summaries", action="store_true",
+                    help="headline line only: skip the batch-8 and other-workload summaries")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--verify-only", action="store_true",
                     help="target model only: prefill, then --steps eager verify passes "
@@ -130,13 +133,23 @@ def verify_bytes(shape, B, K, lens):
     return w_bytes + M * d * e + kv_read + kv_write + M * shape.vocab * 4
 
 
-def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
-    """The oracle (numpy, float64) timed on this host on a bounded sample of the same
-    workload: one round's work for the first layer of the target and of the draft (per
-    layer cost), the LM heads and the accept step, scaled to the full depth."""
-    import dataclasses
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    import torch
+
+def cpu_round_seconds(wl, K, target_seconds):
+    """Seconds of one round of one row for the oracle (numpy, float64) on this host,
+    from a bounded sample: one round's work on the first layer of the target and of the
+    draft, the LM heads and the accept step, repeated for about target_seconds, the
+    per-layer part scaled to the full depth.  Returns (seconds, repetitions)."""
+    import dataclasses
 
     from oracle import model as omodel
     from oracle import philox, sampling
@@ -179,8 +192,8 @@ def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
         t_acc += t3 - t2
         reps += 1
     t_target, t_draft, t_acc = t_target / reps, t_draft / reps, t_acc / reps
-    # a 1-layer forward = embed + 1 layer + head; scale the layer part by depth using a
-    # head-only estimate (the layer count only multiplies the per-layer work)
+    # a 1-layer forward = embed + 1 layer + head; the head-only time separates the part
+    # that the layer count multiplies
     tc.len[:] = ctx
     dc.len[:] = ctx
     t0 = time.perf_counter()
@@ -190,18 +203,35 @@ def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
     for j in range(K):
         omodel.forward(d_shape, Wd, dc, new[:, j:j + 1], layers=0)
     dh = time.perf_counter() - t0
-    round_1row = ((t_target - th) * wl.target.n_layers + th +
-                  (t_draft - dh) * wl.draft.n_layers + dh + t_acc)
-    round_s = round_1row * B
-    cores = len(os.sched_getaffinity(0))
-    value = tokens_per_round / round_s
+    return ((t_target - th) * wl.target.n_layers + th +
+            (t_draft - dh) * wl.draft.n_layers + dh + t_acc), reps
+
+
+def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
+    """The oracle as it stands timed on this host's cores on a bounded sample of the same
+    workload (cpu_round_seconds), twice: with numpy's BLAS on its default threads (the
+    value) and on one thread; both scaled to B rows at the GPU's measured tokens per
+    round."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    half = target_seconds / 2
+    s_all, reps_all = cpu_round_seconds(wl, K, half)
+    with threadpool_limits(limits=1, user_api="blas"):
+        s_one, reps_one = cpu_round_seconds(wl, K, half)
     return {
-        "value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"{reps} repetitions of one round's work on 1 target layer + 1 draft "
-                   f"layer (+ heads, accept step) at context {ctx}, K={K}, one row; "
+        "value": tokens_per_round / (s_all * B), "unit": "tokens/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{reps_all} repetitions of one round's work on 1 target layer + 1 draft "
+                   f"layer (+ heads, accept step) at context {wl.ctx}, K={K}, one row; "
                    f"per-layer time scaled to {wl.target.n_layers}+{wl.draft.n_layers} "
-                   f"layers and {B} rows; numpy float64 with its default BLAS threads; "
-                   f"{round_s:.2f} s per full round"),
+                   f"layers and {B} rows; numpy float64 on {threads} BLAS threads; "
+                   f"{s_all * B:.2f} s per full round"),
+        "single_thread": {"value": tokens_per_round / (s_one * B), "cores": 1,
+                          "repetitions": reps_one, "seconds_per_round": s_one * B},
+        "cpu_model": cpu_model(),
+        "host_cpus_visible": len(os.sched_getaffinity(0)),
     }
 
 
@@ -242,7 +272,7 @@ def verify_only(args, wl):
                       "kernel_sources_sha256": gemm_source_hash()}))
 
 
-def accept_only(args):
+def accept_only(args, emit=True):
     """The accept / resample step alone: target logits [B, K+1, V] ~ N(0, 2^2), draft
     logits = target + N(0, 0.5^2), temperature 0.8, top-k and top-p off, draft tokens
     drawn from the processed draft rows (input synthesis, outside the timed region).
@@ -301,7 +331,7 @@ def accept_only(args):
     vb = (B * (K + 1) * V + B * K * V) * 4  # every logit row read once
     c_med = float(np.median(call_ms))
     achieved = vb / (c_med / 1e3) / 1e9
-    print(json.dumps({
+    res = {
         "metric": "accepted tokens/s + vocab-kernel HBM GB/s (% of peak), accept/resample alone",
         "value": tokens / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
@@ -316,7 +346,10 @@ def accept_only(args):
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "bytes_per_call": vb},
-    }))
+    }
+    if emit:
+        print(json.dumps(res))
+    return res
 
 
 AR_STEPS = 8  # single-token steps per graph of the plain-decoding baseline
@@ -457,6 +490,206 @@ def sweep(args):
                       "top-p 0.95, random-init models"}))
 
 
+def build_models(wl, seed, dev="cuda"):
+    """Target and draft of a workload, each tensor generated on the device, loaded into
+    the model's store and released (peak memory: the stores plus one tensor)."""
+    import torch
+
+    from speculative_decoding_forward_amd import binding, synth
+
+    models = []
+    for shape, mid in ((wl.target, synth.TARGET), (wl.draft, synth.DRAFT)):
+        m = binding.Model(shape, None, device=dev)
+        for nm in shape.weight_names():
+            w = synth.make_weight(shape, nm, seed=seed, model_id=mid, device=dev)
+            m.load_weight(nm, w)
+            del w
+        models.append(m)
+    torch.cuda.synchronize()
+    return models
+
+
+def run_rounds(wl, B, K, steps, warmup, seed, models, timed_extra=0, with_ar=True,
+               gemm_timing=True):
+    """Speculative rounds of a workload on one GPU: prefill, `warmup` eager rounds, one
+    round captured as a HIP graph and replayed `steps` times between two synchronisations
+    (the timed region), then -- outside it -- the verify pass alone, the verify GEMMs'
+    and attention's event-timed launches, plain decoding on the same kernels, and
+    `timed_extra` more replays for a steadier tokens/s.  Returns the measurements."""
+    import torch
+
+    from speculative_decoding_forward_amd import binding, rounds, synth
+
+    knobs = (wl.temperature, wl.top_k, wl.top_p)
+    dev = "cuda"
+    rounds_total = warmup + 1 + steps + timed_extra
+    max_len = wl.ctx + (rounds_total + 1) * (K + 1) + 2 + AR_STEPS
+    dec = rounds.SpecDecoder(wl.target, None, wl.draft, None, B, K, max_len, knobs, seed=seed,
+                             models=models)
+    ctx = synth.context_ids(seed, B, wl.ctx, wl.target.vocab)
+    dec.prefill(ctx)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for r in range(warmup):
+        dec.step(r)
+    torch.cuda.synchronize()
+    # one round captured as a HIP graph, numbered by the device round counter; one replay
+    # and the token accumulation run once before the clock starts (a kernel's first use
+    # loads its code, which is not part of a round); per-round counts land in row i of
+    # n_hist (one elementwise add per round)
+    dec.set_round(warmup)
+    dec.capture()
+    n_hist = torch.zeros((steps + timed_extra, B), dtype=torch.int32, device=dev)
+    dec.replay()
+    n_hist[0] += dec.n_out
+    n_hist.zero_()
+    len_start = dec.tkv.len.cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        dec.replay()
+        n_hist[i] += dec.n_out
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    len_end = dec.tkv.len.cpu().numpy().astype(np.float64)
+    extra = None
+    if timed_extra:
+        t1 = time.perf_counter()
+        for i in range(steps, steps + timed_extra):
+            dec.replay()
+            n_hist[i] += dec.n_out
+        torch.cuda.synchronize()
+        extra = time.perf_counter() - t1
+    hist_all = n_hist.cpu().numpy().astype(np.int64)
+    if timed_extra:
+        extra = {"rounds": timed_extra, "tokens": int(hist_all[steps:].sum()),
+                 "tokens_per_s": float(hist_all[steps:].sum() / extra)}
+    hist = hist_all[:steps]
+    assert hist_all.min() >= 1, "a row emitted nothing (row status set)"
+    tokens = int(hist.sum())
+
+    # verify-pass latency: a graph of [verify-input assembly, verify pass, roll-back to
+    # the pre-verify lengths], replayed with events around each replay
+    saved_len = dec.tkv.len.clone()
+    vg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(vg):
+        dec.verify_phase()
+        dec.tkv.rollback(saved_len)
+    vg.replay()
+    torch.cuda.synchronize()
+    n_v = max(10, min(64, steps))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_v)]
+    for a, b in ev:
+        a.record(stream)
+        vg.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    lens_v = saved_len.cpu().numpy().astype(np.float64)
+    out = {}
+    if gemm_timing:
+        # the verify pass's weight-streaming GEMMs and attention, timed by HIP events
+        # attached to their own dispatch packets over eager verify passes
+        n_meas = max(4, min(20, steps // 2))
+        torch.cuda.synchronize()
+        binding.timing_enable(True)
+        binding.timing_read()
+        for _ in range(n_meas):
+            dec.verify_phase()
+            dec.tkv.rollback(saved_len)
+        torch.cuda.synchronize()
+        binding.timing_enable(False)
+        gemm_ms, gemm_n, attn_ms, attn_n = binding.timing_read()
+        gb_v, gn_v = gemm_bytes_per_verify(wl.target, B * (K + 1))
+        assert gemm_n == n_meas * gn_v, (gemm_n,)
+        gemm_avg_s = gemm_ms / 1e3 / gemm_n
+        achieved = gb_v / gn_v / gemm_avg_s / 1e9
+        out.update(gemm_avg_bytes=gb_v / gn_v, gemm_avg_s=gemm_avg_s, gemm_achieved=achieved,
+                   gemm_n=gemm_n, gemm_ms_per_pass=gemm_ms / n_meas,
+                   attn_ms_per_pass=attn_ms / n_meas,
+                   attn_kv_GBps=sum(wl.target.n_layers * 2 * (l + K + 1) * wl.target.d_model *
+                                    wl.target.elt_bytes() for l in lens_v) / (attn_ms / n_meas / 1e3) / 1e9)
+    acc_counts = hist - 1
+    accepted = int(acc_counts.sum())
+    rejections = int((acc_counts < K).sum())
+    alpha_hat = accepted / max(1, accepted + rejections)
+    e_tokens_iid = (1 - alpha_hat ** (K + 1)) / (1 - alpha_hat) if alpha_hat < 1 else K + 1
+    vb = verify_bytes(wl.target, B, K, lens_v)
+    v_med = float(np.median(verify_ms))
+    out.update(tokens=tokens, wall=wall, hist=hist, len_start=len_start, len_end=len_end,
+               verify_ms=verify_ms, v_med=v_med, vb=vb, alpha=alpha_hat, e_iid=e_tokens_iid,
+               extra=extra)
+    if with_ar:
+        tok0 = torch.full((B, 2), -1, dtype=torch.int32, device=dev)
+        tok0[:, 0] = dec.pending[:, 0]
+        n_ar = max(6, min(steps, 20))
+        t_ar = ar_ms_per_token(binding, torch, dec.target, dec.tkv, dec.ws_t, B,
+                               wl.target.vocab, knobs, seed, tok0, n_ar)
+        d_ar = ar_ms_per_token(binding, torch, dec.draft, dec.dkv, dec.ws_d, B,
+                               wl.target.vocab, knobs, seed, tok0, n_ar)
+        out.update(t_ar=t_ar, d_ar=d_ar, ar_bytes=verify_bytes(wl.target, B, 0, len_end))
+    del dec, vg
+    torch.cuda.empty_cache()
+    return out
+
+
+def summary_line(wl, B, K, r, steps):
+    """The compact per-workload figures of a run_rounds() result."""
+    d = {"workload": wl.name, "batch": B, "K": K, "context": wl.ctx,
+         "tokens_per_s": r["tokens"] / r["wall"], "ms_per_round": r["wall"] / steps * 1e3,
+         "rounds": steps, "alpha_measured": r["alpha"],
+         "tokens_per_round_per_row": r["tokens"] / (B * steps),
+         "verify_ms_median": r["v_med"], "verify_bytes": r["vb"],
+         "verify_frac_of_peak": r["vb"] / (r["v_med"] / 1e3) / 1e9 / HBM_PEAK_GBS}
+    if "gemm_achieved" in r:
+        d.update(gemm_GBps=r["gemm_achieved"], gemm_frac_of_peak=r["gemm_achieved"] / HBM_PEAK_GBS,
+                 gemm_avg_launch_us=r["gemm_avg_s"] * 1e6,
+                 attention_ms_per_pass=r["attn_ms_per_pass"],
+                 attention_frac_of_peak=r["attn_kv_GBps"] / HBM_PEAK_GBS)
+    if "t_ar" in r:
+        c = r["d_ar"] / r["t_ar"]
+        d.update(autoregressive_tokens_per_s=B / (r["t_ar"] / 1e3), c_measured=c,
+                 speedup_measured=(r["tokens"] / r["wall"]) / (B / (r["t_ar"] / 1e3)),
+                 speedup_formula=speedup_formula(r["alpha"], K, c))
+    e08 = (1 - 0.8 ** (K + 1)) / (1 - 0.8)
+    d["projected_tokens_per_s_at_alpha_0.8"] = B * e08 / (r["wall"] / steps)
+    return d
+
+
+def guarded(fn, *a, **kw):
+    """A summary that must never cost the headline line: its result, or its error."""
+    import torch
+    try:
+        return fn(*a, **kw)
+    except Exception as exc:  # noqa: BLE001 -- reported in the JSON line
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return {"error": f"{type(exc).__name__}: {exc}"[:300]}
+
+
+def workload_summary(name, B, K, steps, warmup, seed):
+    import torch
+
+    from speculative_decoding_forward_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    models = build_models(wl, seed)
+    r = run_rounds(wl, B, K, steps, warmup, seed, models, gemm_timing=wl.target.dtype == "bf16")
+    del models
+    gc.collect()
+    torch.cuda.empty_cache()
+    return summary_line(wl, B, K, r, steps)
+
+
+def accept_summary(seed):
+    class A:
+        pass
+    a = A()
+    a.batch, a.K, a.seed, a.steps, a.warmup = None, None, seed, 200, 3
+    return accept_only(a, emit=False)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -466,7 +699,7 @@ def main():
         sys.exit(2)
     import torch
 
-    from speculative_decoding_forward_amd import binding, rounds, synth
+    from speculative_decoding_forward_amd import synth
 
     assert torch.cuda.is_available(), "no GPU"
     if args.calibrate_copy:
@@ -490,117 +723,18 @@ def main():
         return
     B = args.batch or wl.batch
     K = args.K or wl.K
-    knobs = (wl.temperature, wl.top_k, wl.top_p)
-    dev = "cuda"
     torch.manual_seed(args.seed)
-    Wt = synth.make_weights(wl.target, seed=args.seed, model_id=synth.TARGET, device=dev)
-    Wd = synth.make_weights(wl.draft, seed=args.seed, model_id=synth.DRAFT, device=dev)
-    rounds_total = args.warmup + 1 + args.steps  # eager warm-up, graph warm-up, timed
-    max_len = wl.ctx + (rounds_total + 1) * (K + 1) + 2 + AR_STEPS
-    dec = rounds.SpecDecoder(wl.target, Wt, wl.draft, Wd, B, K, max_len, knobs, seed=args.seed)
-    ctx = synth.context_ids(args.seed, B, wl.ctx, wl.target.vocab)
-    dec.prefill(ctx)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    for r in range(args.warmup):
-        dec.step(r)
-    torch.cuda.synchronize()
-
-    # one round captured as a HIP graph, numbered by the device round counter
-    dec.set_round(args.warmup)
-    dec.capture()
-    # one round -- within the cache's capacity -- runs before the clock starts, with the
-    # token accumulation of the timed loop: the first use of a kernel loads its code
-    # (the accumulation's took 20-80 ms), which is not part of a round
-    # (per-round counts land in row i of n_hist: one elementwise add per round, as a
-    # running sum would cost)
-    n_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
-    dec.replay()
-    n_hist[0] += dec.n_out
-    n_hist.zero_()
-    len_start = dec.tkv.len.cpu().numpy().astype(np.float64)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        dec.replay()
-        n_hist[i] += dec.n_out
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    hist = n_hist.cpu().numpy().astype(np.int64)
-    assert hist.min() >= 1, "a row emitted nothing (row status set)"
-    tokens = int(hist.sum())
-    len_end = dec.tkv.len.cpu().numpy().astype(np.float64)
-
-    # verify-pass latency: a graph of [verify-input assembly, verify pass, roll-back to
-    # the pre-verify lengths], replayed with events around each replay
-    saved_len = dec.tkv.len.clone()
-    vg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(vg):
-        dec.verify_phase()
-        dec.tkv.rollback(saved_len)
-    vg.replay()  # first launch outside the measurement, as above
-    torch.cuda.synchronize()
-    n_v = max(10, min(64, args.steps))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_v)]
-    for a, b in ev:
-        a.record(stream)
-        vg.replay()
-        b.record(stream)
-    torch.cuda.synchronize()
-    verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
-
-    # dominant kernel: the verify pass's weight-streaming GEMM, timed by HIP events
-    # attached to its own dispatch packets (hipExtLaunchKernelGGL) over eager verify
-    # passes, each rolled back to the same cache length
-    n_meas = max(4, min(20, args.steps // 2))
-    torch.cuda.synchronize()
-    binding.timing_enable(True)
-    binding.timing_read()
-    for i in range(n_meas):
-        dec.verify_phase()
-        dec.tkv.rollback(saved_len)
-    torch.cuda.synchronize()
-    binding.timing_enable(False)
-    gemm_ms, gemm_n, attn_ms, attn_n = binding.timing_read()
-
-    R_v = B * (K + 1)
-    gb_v, gn_v = gemm_bytes_per_verify(wl.target, R_v)
-    assert gemm_n == n_meas * gn_v, (gemm_n,)
-    gemm_avg_bytes = gb_v / gn_v
-    gemm_avg_s = gemm_ms / 1e3 / gemm_n
-    achieved = gemm_avg_bytes / gemm_avg_s / 1e9
-    vb = verify_bytes(wl.target, B, K, (len_start + len_end) / 2)
-    v_med = float(np.median(verify_ms))
-    # acceptance rate as the pages define it: the probability that a draft passes, given
-    # that every earlier one did ([LENS] §3.1: beta per position, alpha its expectation,
-    # i.i.d. in the tokens-per-run formula), estimated as accepted / (accepted +
-    # rejections); a round with all K accepted has no rejection
-    acc_counts = hist - 1
-    accepted = int(acc_counts.sum())
-    rejections = int((acc_counts < K).sum())
-    alpha_hat = accepted / max(1, accepted + rejections)
-    e_tokens_iid = (1 - alpha_hat ** (K + 1)) / (1 - alpha_hat) if alpha_hat < 1 else K + 1
-
-    # plain decoding on the same kernels: the target's and the draft's one-token steps
-    tok0 = torch.full((B, 2), -1, dtype=torch.int32, device=dev)
-    tok0[:, 0] = dec.pending[:, 0]
-    n_ar = max(6, min(args.steps, 20))
-    t_ar = ar_ms_per_token(binding, torch, dec.target, dec.tkv, dec.ws_t, B, wl.target.vocab,
-                           knobs, args.seed, tok0, n_ar)
-    d_ar = ar_ms_per_token(binding, torch, dec.draft, dec.dkv, dec.ws_d, B, wl.target.vocab,
-                           knobs, args.seed, tok0, n_ar)
+    models = build_models(wl, args.seed)
+    r = run_rounds(wl, B, K, args.steps, args.warmup, args.seed, models, timed_extra=200,
+                   gemm_timing=wl.target.dtype == "bf16")
+    tokens, wall = r["tokens"], r["wall"]
+    round_s = wall / args.steps
+    t_ar, d_ar = r["t_ar"], r["d_ar"]
     c_hat = d_ar / t_ar
     ar_tps = B / (t_ar / 1e3)
-    round_s = wall / args.steps
-    # the pages' expected wall-time improvement ([LENS] "How much faster in practice?",
-    # [ZSM] "How much faster"): tokens per run over the cost of K draft runs + one
-    # target run, in units of a target run
-    formula = e_tokens_iid / (K * c_hat + 1)
-    ar_bytes = verify_bytes(wl.target, B, 0, len_end)  # one token per row, weights once
+    formula = r["e_iid"] / (K * c_hat + 1)
     e08 = (1 - 0.8 ** (K + 1)) / (1 - 0.8)
+    vb, v_med, verify_ms = r["vb"], r["v_med"], r["verify_ms"]
     res = {
         "metric": "accepted tokens/s + verify-pass HBM GB/s (% of peak), 7B-shape bf16, K=5",
         "value": tokens / wall,
@@ -627,8 +761,8 @@ def main():
         "verify_frac_of_peak": vb / (v_med / 1e3) / 1e9 / HBM_PEAK_GBS,
         "verify_bytes": vb,
         "tokens_per_round_per_row": tokens / (B * args.steps),
-        "alpha_measured": alpha_hat,
-        "tokens_per_round_at_alpha_iid": e_tokens_iid,
+        "alpha_measured": r["alpha"],
+        "tokens_per_round_at_alpha_iid": r["e_iid"],
         "autoregressive": {
             "what": "plain decoding on the same kernels: one-token target steps (forward + "
                     "sample), graph of 8 steps, median of HIP-event-timed replays",
@@ -636,8 +770,8 @@ def main():
             "draft_ms_per_token": d_ar, "c_measured": c_hat,
             "speedup_measured": (tokens / wall) / ar_tps,
             "speedup_formula_at_measured_alpha_c": formula,
-            "bandwidth_ceiling_tokens_per_s": B * HBM_PEAK_GBS * 1e9 / ar_bytes,
-            "bytes_per_token_step": ar_bytes,
+            "bandwidth_ceiling_tokens_per_s": B * HBM_PEAK_GBS * 1e9 / r["ar_bytes"],
+            "bytes_per_token_step": r["ar_bytes"],
         },
         "projected_at_alpha_0.8": {
             "note": "context, not measured: the measured round time with the tokens per "
@@ -645,17 +779,36 @@ def main():
             "tokens_per_s": B * e08 / round_s,
             "speedup_vs_measured_autoregressive": B * e08 / round_s / ar_tps,
         },
-        "verify_attention_ms": attn_ms / n_meas,
-        "verify_gemm_ms": gemm_ms / n_meas,
+        "verify_attention_ms": r["attn_ms_per_pass"],
+        "verify_attention_frac_of_peak": r["attn_kv_GBps"] / HBM_PEAK_GBS,
+        "verify_gemm_ms": r["gemm_ms_per_pass"],
         "roofline": {"bound": "hbm",
                      "kernel": "k_gemm_bf16 (verify-pass weight-streaming GEMM, 4 per layer "
                                "+ LM head)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                     "bytes_per_launch": gemm_avg_bytes,
-                     "avg_launch_us": gemm_avg_s * 1e6, "launches": gemm_n,
+                     "achieved": r["gemm_achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["gemm_achieved"] / HBM_PEAK_GBS, "traffic": recorded_traffic(),
+                     "bytes_per_launch": r["gemm_avg_bytes"],
+                     "avg_launch_us": r["gemm_avg_s"] * 1e6, "launches": r["gemm_n"],
                      "kernel_sources_sha256": gemm_source_hash()},
     }
+    if r["extra"]:
+        res["tokens_per_s_over_more_rounds"] = dict(
+            r["extra"], note="context: the same graph replayed right after the timed rounds "
+                             "(tokens per round vary round to round at B = 1)")
+    if not args.no_summaries and args.workload == "7b" and B == 1:
+        # batch 8 on the same models (its rows add KV reads and GEMM rows, not weights)
+        res["b8"] = guarded(lambda: summary_line(wl, 8, K, run_rounds(
+            wl, 8, K, max(20, args.steps), 2, args.seed, models), max(20, args.steps)))
+    del models
+    gc.collect()
+    torch.cuda.empty_cache()
+    if not args.no_summaries and args.workload == "7b" and B == 1:
+        res["other_configs"] = {
+            "tiny": guarded(workload_summary, "tiny", 1, 4, 32, 2, args.seed),
+            "small": guarded(workload_summary, "small", 1, 4, 100, 2, args.seed),
+            "accept": guarded(accept_summary, args.seed),
+            "70b": guarded(workload_summary, "70b", 1, 4, 20, 2, args.seed),
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, B, K, tokens / args.steps, args.cpu_seconds)
     print(json.dumps(res))
