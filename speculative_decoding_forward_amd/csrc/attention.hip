@@ -15,9 +15,14 @@
 // Every wave load is therefore 1 KB contiguous.
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
-// (b, h) and one group of up to 16 queries; the split count makes the grid at most one
-// workgroup per compute unit and leaves each split about 1.5 blocks per wave
-// (attn_nsplit).  Its waves (8 for head_dim 128) take the blocks
+// (b, h) and one group of up to 16 queries.  The split count (the grid) is fixed per
+// launch shape -- at most one workgroup per compute unit, about 1.5 blocks per wave over
+// the cache capacity (attn_nsplit) -- and each row divides its ACTUAL blocks over it:
+// bps = max(ceil(blocks / splits), waves), read on the device from the row's length, so
+// a row far shorter than the capacity still spreads over every split (a split count
+// taken from the capacity left 3 of 8 splits idle at 2048 of 3456 positions: 15.6 against
+// 13.5 us per launch), and no split has less than one block per wave.  Its waves (8 for
+// head_dim 128) take the blocks
 // round-robin, keep two blocks of K and V in flight each -- with a split's blocks thus
 // all requested at once -- and run an online softmax per query.  The
 // wave states merge in LDS; with more than one split the workgroup partial goes to
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     const u16* __restrict__ q, int M, int H, const u16* __restrict__ kc,
     const u16* __restrict__ vc, size_t row_stride, size_t head_stride,
     const int32_t* __restrict__ pos0, const int32_t* __restrict__ ntok_eff,
-    float* __restrict__ part, unsigned* __restrict__ counters, int nsplit, int bps,
+    float* __restrict__ part, unsigned* __restrict__ counters, int nsplit,
     u16* __restrict__ out) {
   constexpr int NS = HD / 32;  // K slices (MFMAs per 16-key tile)
   constexpr int NT = HD / 16;  // dim tiles of O
@@ -74,9 +79,10 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   const int nq = ntok_eff[b];
   const int p0 = pos0[b];
   const int len_end = p0 + nq;
+  const int nblk = cdiv(len_end, AKB);
+  const int bps = max(cdiv(nblk, nsplit), AW);  // blocks per split of this row
   // blocks of this wave in its split: wv, wv + AW, ... below bps
   const int nmine = wv < bps ? (bps - 1 - wv) / AW + 1 : 0;
-  const int nblk = cdiv(len_end, AKB);
   const int n_active = cdiv(nblk, bps);
   const int d = H * HD;
   const int jend = min(M, qg * AQ + AQ);  // rows of this query group
@@ -345,11 +351,11 @@ int attn_max_splits(int B, int H, int M, int max_len) {
 
 // Splits per (row, head, query group): as many as make the grid one workgroup per
 // compute unit (a CU holding two workgroups streams its two shares at half the rate
-// and finishes last), but no more than give each split about 1.5 blocks per wave
-// (kAttnBlocksPerSplit): more, smaller splits only lengthen the merge.  Over a 69-block
-// capacity, 8 or 14 splits (9 or 5 blocks) took 14.2 / 11.1 us at 6 / 1 queries per
-// row, 6 splits of 12 blocks 13.6 / 10.6 us, 5 of 16 and 3 of 24 longer again.  A split
-// takes `bps` consecutive blocks (attn_bps), the workgroup's waves round-robin.
+// and finishes last), but no more than give each split about 1.5 blocks per wave of the
+// capacity (kAttnBlocksPerSplit): more, smaller splits only lengthen the merge.  Over a
+// 69-block capacity, 8 or 14 splits (9 or 5 blocks) took 14.2 / 11.1 us at 6 / 1
+// queries per row, 6 splits of 12 blocks 13.6 / 10.6 us, 5 of 16 and 3 of 24 longer
+// again.  The kernel divides each row's actual blocks over these splits.
 constexpr int kAttnBlocksPerSplit = 3 * SPEC_ATTN_WAVES / 2;
 int attn_nsplit(int B, int H, int M, int max_len) {
   const int blocks = cdiv(max_len, AKB), groups = B * H * cdiv(M, AQ);
@@ -362,10 +368,6 @@ int attn_nsplit(int B, int H, int M, int max_len) {
   return cdiv(blocks, bps);
 }
 
-int attn_bps(int B, int H, int M, int max_len) {
-  return cdiv(cdiv(max_len, AKB), attn_nsplit(B, H, M, max_len));
-}
-
 int attn_groups(int M) { return cdiv(M, AQ); }
 
 hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, size_t row_stride,
@@ -373,17 +375,16 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
                                  const int32_t* pos0, const int32_t* ntok_eff, float* part,
                                  unsigned* counters, int max_len, u16* out, hipStream_t s,
                                  hipEvent_t e0, hipEvent_t e1) {
-  const int bps = attn_bps(B, H, M, max_len);
   const int nsplit = attn_nsplit(B, H, M, max_len);
   const dim3 grid(nsplit, H, B * attn_groups(M));
   if (hd == 128)
     hipExtLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(attn_waves<128>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
                           vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          bps, out);
+                          out);
   else if (hd == 64)
     hipExtLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(attn_waves<64>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
                           vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          bps, out);
+                          out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
