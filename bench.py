@@ -207,6 +207,84 @@ def cpu_round_seconds(wl, K, target_seconds):
             (t_draft - dh) * wl.draft.n_layers + dh + t_acc), reps
 
 
+def cpu_verify_seconds(wl, K):
+    """Seconds of one oracle verify forward (K+1 new tokens, one row, at the workload's
+    context) and the repetitions behind it: the first layer of the target timed, the
+    layer part scaled to the full depth (the tiny model runs whole)."""
+    import dataclasses
+
+    from oracle import model as omodel
+    from speculative_decoding_forward_amd import synth
+
+    L = wl.target.n_layers
+    shape = wl.target if L <= 2 else dataclasses.replace(wl.target, n_layers=1)
+    W = synth.weights_to_numpy(synth.make_weights(shape, seed=0, device="cpu"))
+    c = omodel.KVCache(shape, 1, wl.ctx + K + 2)
+    c.fill(synth.kv_fill(shape, 1, wl.ctx + K + 2, wl.ctx, seed=0).float().numpy(), [wl.ctx])
+    new = np.random.default_rng(0).integers(0, shape.vocab, (1, K + 1))
+    reps, t = 0, 0.0
+    while reps < 2 or (t < 1.0 and reps < 20):
+        c.len[:] = wl.ctx
+        t0 = time.perf_counter()
+        omodel.forward(shape, W, c, new)
+        t += time.perf_counter() - t0
+        reps += 1
+    t /= reps
+    if shape is wl.target:
+        return t, reps
+    c.len[:] = wl.ctx
+    t0 = time.perf_counter()
+    omodel.forward(shape, W, c, new, layers=0)
+    th = time.perf_counter() - t0
+    return (t - th) * L + th, reps
+
+
+def cpu_accept_seconds():
+    """Seconds of one oracle accept / resample call over the accept-only workload
+    (B = 32 rows, K = 8, V = 32000, T = 0.8)."""
+    from oracle import philox, sampling
+    from speculative_decoding_forward_amd import synth
+
+    B, K, T = 32, 8, 0.8
+    p, q = synth.vocab_logits(0, B, K, 32000, 2.0, 0.5)
+    xt = np.zeros((B, K), dtype=np.int64)
+    t0 = time.perf_counter()
+    for b in range(B):
+        sampling.accept_resample_logits(p[b], q[b], xt[b], philox.uniform(0, 0, np.arange(K), b, 1),
+                                        philox.uniform(0, 0, np.arange(K + 1), b, 2), T, 0, 1.0)
+    return time.perf_counter() - t0
+
+
+def cpu_items(K=5):
+    """The oracle's verify forward per workload and its accept step, on numpy's default
+    BLAS threads and on one thread (seconds per call; the 70B and 7B figures scale one
+    timed layer to the full depth)."""
+    from threadpoolctl import threadpool_limits
+
+    from speculative_decoding_forward_amd import synth
+
+    out = {}
+    for threads in ("all", "one"):
+        res = {}
+        ctx = threadpool_limits(limits=1, user_api="blas") if threads == "one" else None
+        try:
+            if ctx:
+                ctx.__enter__()
+            for name in ("tiny", "small", "7b", "70b"):
+                wl = synth.WORKLOADS[name]
+                s, reps = cpu_verify_seconds(wl, wl.K if name != "7b" else K)
+                res[f"verify_{name}_s"] = s
+            res["accept_b32_k8_s"] = cpu_accept_seconds()
+        finally:
+            if ctx:
+                ctx.__exit__(None, None, None)
+        out[threads] = res
+    out["note"] = ("oracle seconds per call: one verify forward over K+1 tokens at each "
+                   "workload's context (one row; small, 7B and 70B from one timed layer scaled "
+                   "to the full depth), and one accept step over the 32 x 9 x 32000 workload")
+    return out
+
+
 def cpu_baseline(wl, B, K, tokens_per_round, target_seconds):
     """The oracle as it stands timed on this host's cores on a bounded sample of the same
     workload (cpu_round_seconds), twice: with numpy's BLAS on its default threads (the
@@ -811,6 +889,8 @@ def main():
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, B, K, tokens / args.steps, args.cpu_seconds)
+        if not args.no_summaries:
+            res["cpu_baseline"]["per_call"] = guarded(cpu_items, K)
     print(json.dumps(res))
 
 
