@@ -94,8 +94,10 @@ struct FwdWS {
   int32_t* ntok_eff;
   int32_t* tok_eff;
   int32_t* ntok2;     // draft-step counts [B]
-  unsigned* counters; // completion counters: [B*H] attention + 1 GEMM
+  unsigned* counters; // completion counters: attention, residual GEMM groups, zeros
   int n_counters;
+  int n_sk;           // residual GEMM group counters
+  float* sk_part;     // residual GEMM slot partials
   float* x;           // residual stream [R, d] fp32
   float* xg;          // bf16: x * g_f after the last layer (act32_index order)
   void* h;            // normed activations [R, d]
@@ -130,9 +132,12 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.tok_eff = (int32_t*)take(R * 4);
   w.ntok2 = (int32_t*)take(B * 4);
   // attention completion counters (one per (row, head, query group), kAttnCounterStride
-  // words apart) followed by 64 zero words; prep clears all of them at the start of
+  // words apart), the residual GEMMs' group counters (one per 4 column tiles,
+  // kSkCounterStride apart) and 64 zero words; prep clears all of them at the start of
   // every forward
-  w.n_counters = B * c.n_heads * attn_groups(M) * kAttnCounterStride + 64;
+  w.n_sk = c.dtype == SPEC_DT_BF16 ? c.d_model / 64 : 0;
+  w.n_counters = B * c.n_heads * attn_groups(M) * kAttnCounterStride +
+                 w.n_sk * kSkCounterStride + 64;
   w.counters = (unsigned*)take((size_t)w.n_counters * 4);
   w.x = (float*)take(R * d * 4);
   w.xg = (float*)take(c.dtype == SPEC_DT_BF16 ? (size_t)act_rows(R) * d * 4 : 0);
@@ -147,6 +152,8 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
                             : 0);
   w.logits = (float*)take(R * V * 4);
   w.ss = (float*)take(c.dtype == SPEC_DT_BF16 ? R * (d / 16) * 4 : 0);
+  // slot partials of the residual GEMMs at 2-4 row tiles: [d/16 tiles][4 slots][4][1 KB]
+  w.sk_part = (float*)take(c.dtype == SPEC_DT_BF16 ? (d / 16) * 4 * 4 * 1024 : 0);
   w.rowscale = (float*)take(c.dtype == SPEC_DT_F32 ? R * 4 : 0);
   w.rope_rows = (double*)take(c.dtype == SPEC_DT_BF16 ? R * c.head_dim * 8 : 0);
   w.total = off;
@@ -300,6 +307,8 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
   base.head_stride = kv->head_stride;
   base.max_len = kv->max_len;
   base.zeros = (const uint16_t*)(w.counters + w.n_counters - 64);
+  base.sk_part = w.sk_part;
+  base.sk_counters = w.counters + (w.n_counters - 64 - w.n_sk * kSkCounterStride);
   base.ss_np = d / 16;
   base.eps = c.norm_eps;
   for (int l = 0; l < c.n_layers; ++l) {

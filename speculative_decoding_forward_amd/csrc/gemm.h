@@ -50,7 +50,14 @@ struct GemmArgs {
   uint16_t* h_out;
   float* xg_out;
   float* ss_out;
+  // RESID at 2-4 row tiles with one tile per workgroup (k_gemm_sk): fp32 slot partials
+  // [ntiles][4][row tiles][64 lanes][4] and completion counters [ntiles / 4] kSkCounterStride
+  // words apart, zero at launch (the last workgroup of a group resets its counter); NULL:
+  // that kernel is not used
+  float* sk_part;
+  unsigned* sk_counters;
 };
+constexpr int kSkCounterStride = 32;  // 128 bytes between completion counters
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // h = bf16(xg * s_r) in the packed bf16 order for R rows of width K (xg in act32_index

@@ -858,6 +858,156 @@ __host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode, int np, b
   return b;
 }
 
+// ------------------------------------------------------ split by wave slot (RESID) --
+//
+// The residual GEMMs (O-projection, down) of a 2-4-row-tile launch on a grid where every
+// workgroup would own a single 16-column tile: the tile-at-a-time kernel then reads the
+// whole A operand (all rows, all K) once per tile, 3 KB of A per KB of weights at 48 rows,
+// and that A traffic from L2 -- not the weight stream -- set its time (with A read from a
+// cached zero block instead, wo + down took 0.95 instead of 1.52 ms per 48-row pass).
+//
+// Here a workgroup owns four tiles (one per streaming wave) and ONE of the four wave
+// slots of k_gemm_bf16: slot q accumulates super-steps q, q + 4, ... of each tile in
+// increasing order, exactly the sequence wave q of k_gemm_bf16 accumulates.  A step's A
+// fragments (all row tiles) are loaded once into LDS, by direct loads split over the
+// waves, and shared by the four tiles -- a quarter of the A traffic per weight byte.  The
+// four slot workgroups of a tile group store their fp32 partials (device-coherent); the
+// last to finish (completion counter, reset by it) sums the slots in order 0..3 and runs
+// the residual epilogue, so every output is bitwise that of k_gemm_bf16.
+constexpr int SK_SLOTS = GW;  // wave slots of the reference summation order
+
+#ifndef SPEC_SK_DEPTH
+#define SPEC_SK_DEPTH 2  // steps requested ahead of the one being multiplied
+#endif
+template <int MT>
+__global__ __launch_bounds__(GT) void k_gemm_sk(GemmArgs g) {
+  static_assert(MT >= 2 && MT <= 4, "2-4 row tiles");
+  constexpr int P = SPEC_SK_DEPTH;  // steps in flight ahead of the multiplied one
+  constexpr int NB = P + 1;         // A buffers (LDS) and W buffers (registers)
+  __shared__ uint4 abuf[NB][MT][4][64];               // A fragments of NB steps
+  __shared__ floatx4 part[GW][SK_SLOTS][MT][64];      // merger: [tile of wave][slot][mt][lane]
+  __shared__ int2 rowinfo[MT * 16];
+  __shared__ double rowscale[MT * 16];
+  __shared__ int is_last;
+  extern __shared__ float4 epi_dyn[];                 // [4 tiles] residual slices + gains
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int grp = blockIdx.x / SK_SLOTS, q = blockIdx.x % SK_SLOTS;
+  const int nsuper = g.K >> 7;
+  const int S = q < nsuper ? (nsuper - 1 - q) / SK_SLOTS + 1 : 0;  // this slot's steps
+  const int rows = min(MT * 16, g.R);
+  float* xres = reinterpret_cast<float*>(epi_dyn);
+  float* gain = xres + GW * MT * 16 * 16;
+  floatx4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (wv == GW) {
+    // the residual slices and gains of the group's tiles, in case this workgroup merges
+    for (int w = 0; w < GW; ++w)
+      lds_copy_resid(g, grp * GW + w, 0, rows, xres + w * MT * 16 * 16, gain + w * 16, lane);
+    for (int i = 0; i < S; ++i) __builtin_amdgcn_s_barrier();  // the streaming waves' steps
+    wait_vm();
+  } else if (S > 0) {
+    const int t = grp * GW + wv;
+    const size_t tile_bytes = (size_t)nsuper * 4096;
+    const uint32_t a_bytes = (uint32_t)act_rows(g.R) * (uint32_t)g.K * 2u;
+    const __amdgpu_buffer_rsrc_t ra = coherent_rsrc(g.A, a_bytes);
+    const __amdgpu_buffer_rsrc_t rw = coherent_rsrc(g.W, (size_t)g.ntiles * tile_bytes);
+    const int nl = lane & 15, gq = lane >> 4;
+    bf16x8 wf[NB][4];
+    // Requests of step i (clamped to the last step: the tail re-reads in-bounds data that
+    // is never multiplied, so every step issues the same MT + 4 loads and one vmcnt value
+    // fits all): this wave's slice (wv) of every row tile's A fragment into LDS buffer
+    // i % NB -- lane l's 16 bytes land at 16 l of the slice, the MFMA A-operand lane order
+    // -- then the tile's 4 weight loads into register buffer i % NB.
+    auto request = [&](int b, int i) {
+      const int js = q + SK_SLOTS * min(i, S - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        buffer_to_lds16(ra, &abuf[b][mt][wv][0],
+                        (uint32_t)(mt * nsuper + js) * 4096u + 1024u * wv + 16u * (4 * nl + gq), 0);
+      const uint32_t so = (uint32_t)((size_t)t * tile_bytes) + (uint32_t)js * 4096u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        wf[b][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane + 1024u * s, so, 2));
+    };
+    auto step = [&](int b, int i) {
+      // step i's A slice and weights have landed once only the P - 1 later steps' loads
+      // may be outstanding; the barrier then makes every wave's slice of A(i) visible and
+      // proves that step i - 1's buffer, (i + P) % NB, has been read by every wave
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (P == 1) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if constexpr (P == 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(MT + 4) : "memory");
+      else __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (MT + 4)) : "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      request((b + P) % NB, i + P);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 af[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          af[mt][s] = __builtin_bit_cast(bf16x8, abuf[b][mt][s][lane]);
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt][s], wf[b][s], acc[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) request(i, i);
+    for (int i0 = 0; i0 < S; i0 += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (i0 + u < S) step(u, i0 + u);
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if (wv < GW) {
+    const int t = grp * GW + wv;
+    // this slot's partial of the wave's tile (zeros for a slot without steps)
+    const __amdgpu_buffer_rsrc_t rp =
+        coherent_rsrc(g.sk_part, (size_t)g.ntiles * SK_SLOTS * MT * 1024);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          acc[mt], rp, (uint32_t)(((t * SK_SLOTS + q) * MT + mt) * 1024 + 16 * lane), 0,
+          kCoherentSc1);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();  // partials stored, residual slices staged
+  if (threadIdx.x == 0)
+    is_last = atomicAdd(&g.sk_counters[grp * kSkCounterStride], 1u) == SK_SLOTS - 1;
+  __syncthreads();
+  if (!is_last) return;
+  if (wv == GW) {
+    if (lane == 0) g.sk_counters[grp * kSkCounterStride] = 0u;
+    return;
+  }
+  // merge: each streaming wave finishes its own tile from the four slot partials
+  const int t = grp * GW + wv;
+  const __amdgpu_buffer_rsrc_t rp =
+      coherent_rsrc(g.sk_part, (size_t)g.ntiles * SK_SLOTS * MT * 1024);
+#pragma unroll
+  for (int qq = 0; qq < SK_SLOTS; ++qq)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      part[wv][qq][mt][lane] =
+          qq == q ? acc[mt]
+                  : __builtin_amdgcn_raw_buffer_load_b128(
+                        rp, (uint32_t)(((t * SK_SLOTS + qq) * MT + mt) * 1024 + 16 * lane), 0,
+                        kCoherentSc1);
+  wave_lds_sync();
+  EpiLds L{};
+  L.xres = xres + wv * MT * 16 * 16;
+  L.gain = gain + wv * 16;
+  gemm_tile_epilogue<MT>(g, t, 0, part[wv], rowinfo, rowscale, L, lane);
+}
+
 // ------------------------------------------------------------------ normalise pass --
 
 // h = bf16(xg * s_r): the LM head's input, RMSNorm(x) * g rounded once after the row
@@ -999,6 +1149,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
+  if (g.mode == EPI_RESID && mt >= 2 && rowblocks == 1 && g.ntiles % SK_SLOTS == 0 &&
+      g.ntiles <= gmax && g.sk_part && g.sk_counters) {
+    // residual products owning one tile per workgroup: four tiles per workgroup, one wave
+    // slot each, A shared across the tiles
+    const unsigned lds = (unsigned)(GW * (mt * 16 * 16 * 4 + 16 * 4));
+    if (mt == 2)
+      hipExtLaunchKernelGGL(k_gemm_sk<2>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
+    else if (mt == 3)
+      hipExtLaunchKernelGGL(k_gemm_sk<3>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
+    else
+      hipExtLaunchKernelGGL(k_gemm_sk<4>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
+    return hipGetLastError();
+  }
   {
     // several row tiles and several tiles per workgroup: the K-outer kernel, in chunks
     // of equal size, at most ko_tpw_max tiles and as many as its LDS allows

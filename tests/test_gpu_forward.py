@@ -224,11 +224,14 @@ def test_draft_steps_match_oracle(B, n_in):
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, None), ("7b", 1, None), ("7b", 8, None),
-                                         ("7b", 8, 3)])
+                                         ("7b", 8, 3), ("7b", 8, 7), ("small", 8, 5)])
 def test_verify_equals_single_token_calls_bitwise(wl_name, B, K):
     """At full size: one call over K+1 positions gives bitwise the logits of K+1
     one-token calls (the premise of the verify pass), and the appended cache entries
-    are bitwise equal; repeating the call is bitwise deterministic."""
+    are bitwise equal; repeating the call is bitwise deterministic.  At B = 8 the verify
+    rows span 2, 3 and 4 row tiles (32, 48 and 64 rows), where the residual products run
+    split by wave slot over four-tile workgroups (8 rows of one-token calls: one row tile,
+    tile at a time); the small model's residual products have 128 tiles (32 groups)."""
     wl = synth.WORKLOADS[wl_name]
     K = K or wl.K
     shape = wl.target
