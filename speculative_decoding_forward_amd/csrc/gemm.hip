@@ -38,6 +38,13 @@
 // rounding of the input falls before the row factor instead of after it).  The LM head
 // takes bf16(RMSNorm(x) * g) from launch_norm_pack, the rounding after the row factor.
 //
+// Kernels by row count: k_gemm_bf16 (one row tile; and several row tiles with one tile
+// group per workgroup), k_gemm_bf16_ko (2-4 row tiles, several tiles per workgroup: A loaded
+// once per step for a chunk of tiles), k_gemm_sk (residual products at 2-4 row tiles that
+// would own one tile per workgroup: four tiles per workgroup, split by wave slot).  All
+// three accumulate every output element over the same steps in the same order, so a verify
+// call equals single-token calls bit for bit.
+//
 // fp32 path (small fp32 models): separate simple kernels, one wave per output column.
 #include <hip/hip_ext.h>
 
