@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="K x batch sweep on the 7B shape (one JSON line per point, then a "
                          "summary line); --steps timed rounds per point")
-    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64")
     ap.add_argument("--sweep-K", default="1,2,3,4,5,6,7,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-summaries", action="store_true",
