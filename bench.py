@@ -877,6 +877,10 @@ def main():
         # batch 8 on the same models (its rows add KV reads and GEMM rows, not weights)
         res["b8"] = guarded(lambda: summary_line(wl, 8, K, run_rounds(
             wl, 8, K, max(20, args.steps), 2, args.seed, models), max(20, args.steps)))
+        # the other draft lengths of the headline workload, batch 1, on the same models
+        n_k = max(20, min(args.steps, 60))
+        res["other_K"] = {f"K{k}": guarded(lambda k=k: summary_line(
+            wl, 1, k, run_rounds(wl, 1, k, n_k, 2, args.seed, models), n_k)) for k in (3, 7)}
     del models
     gc.collect()
     torch.cuda.empty_cache()
