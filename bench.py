@@ -568,6 +568,29 @@ def sweep(args):
                       "top-p 0.95, random-init models"}))
 
 
+def device_copy_GBps(mib=1024, reps=10):
+    """Context for the roofline: the HBM rate of torch's device-to-device copy of `mib` MiB
+    (bytes read + bytes written over the median event-timed copy)."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms / 1e3) / 1e9
+
+
 def build_models(wl, seed, dev="cuda"):
     """Target and draft of a workload, each tensor generated on the device, loaded into
     the model's store and released (peak memory: the stores plus one tensor)."""
@@ -869,6 +892,7 @@ def main():
                      "avg_launch_us": r["gemm_avg_s"] * 1e6, "launches": r["gemm_n"],
                      "kernel_sources_sha256": gemm_source_hash()},
     }
+    res["device_copy_GBps"] = guarded(device_copy_GBps)
     if r["extra"]:
         res["tokens_per_s_over_more_rounds"] = dict(
             r["extra"], note="context: the same graph replayed right after the timed rounds "
