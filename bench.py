@@ -669,14 +669,19 @@ def run_rounds(wl, B, K, steps, warmup, seed, models, timed_extra=0, with_ar=Tru
     assert hist_all.min() >= 1, "a row emitted nothing (row status set)"
     tokens = int(hist.sum())
 
-    # verify-pass latency: a graph of [verify-input assembly, verify pass, roll-back to
-    # the pre-verify lengths], replayed with events around each replay
+    # verify-pass latency: a graph of [verify-input assembly, verify pass] replayed with
+    # events around each replay, and after each, outside the events, a graph rolling the
+    # cache back to the pre-verify lengths
     saved_len = dec.tkv.len.clone()
     vg = torch.cuda.CUDAGraph()
     with torch.cuda.graph(vg):
         dec.verify_phase()
+    rg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rg):
         dec.tkv.rollback(saved_len)
+    dec.tkv.rollback(saved_len)
     vg.replay()
+    rg.replay()
     torch.cuda.synchronize()
     n_v = max(10, min(64, steps))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -685,6 +690,7 @@ def run_rounds(wl, B, K, steps, warmup, seed, models, timed_extra=0, with_ar=Tru
         a.record(stream)
         vg.replay()
         b.record(stream)
+        rg.replay()
     torch.cuda.synchronize()
     verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
     lens_v = saved_len.cpu().numpy().astype(np.float64)
@@ -730,7 +736,7 @@ def run_rounds(wl, B, K, steps, warmup, seed, models, timed_extra=0, with_ar=Tru
         d_ar = ar_ms_per_token(binding, torch, dec.draft, dec.dkv, dec.ws_d, B,
                                wl.target.vocab, knobs, seed, tok0, n_ar)
         out.update(t_ar=t_ar, d_ar=d_ar, ar_bytes=verify_bytes(wl.target, B, 0, len_end))
-    del dec, vg
+    del dec, vg, rg
     torch.cuda.empty_cache()
     return out
 
