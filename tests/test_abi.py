@@ -101,3 +101,46 @@ def _load_missing(tmp_path):
         binding.load(str(tmp_path / "missing.so"))
     finally:
         binding._LIB = saved
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "specdec.h"
+int main(void) {
+  spec_model_cfg cfg;
+  memset(&cfg, 0, sizeof cfg);
+  cfg.n_layers = 2; cfg.d_model = 256; cfg.n_heads = 2; cfg.head_dim = 128;
+  cfg.d_ffn = 512; cfg.vocab = 1024; cfg.ffn_kind = SPEC_FFN_SWIGLU; cfg.dtype = SPEC_DT_BF16;
+  cfg.norm_eps = 1e-5f; cfg.rope_theta = 10000.0f;
+  size_t m = spec_model_bytes(&cfg), w = spec_workspace_bytes(&cfg, 2, 6, 128);
+  spec_model* h = 0;
+  int bad = spec_model_create(&cfg, 0, m, &h);  /* null store: rejected, nothing launched */
+  printf("%d %zu %zu %d %s\n", spec_abi_version(), m, w, bad, spec_status_str(bad));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/specdec.h compiles as C11 with warnings as errors, and a C program links
+    against the library and calls its host-side queries (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi.c"
+    exe = tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    lib_dir = os.path.dirname(binding.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-I", os.path.dirname(HEADER), str(src), "-o", str(exe),
+                        "-L", lib_dir, "-lspecdec", f"-Wl,-rpath,{lib_dir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr[-2000:]
+    ver, m, w, bad, msg = out.stdout.split(maxsplit=4)
+    assert int(ver) == 2 and int(m) > 0 and int(w) > 0
+    assert int(bad) == binding.SPEC_E_INVALID
