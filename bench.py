@@ -855,10 +855,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.target.dtype == "bf16" else "f32",
         "data": "synthetic: seeded random-init weights (N(0,0.02^2)), uniform context ids",
-        "config": {"workload": f"{args.workload}-shape speculative rounds",
-                   "target": f"L{wl.target.n_layers} d{wl.target.d_model} "
-                             f"F{wl.target.d_ffn} {wl.target.ffn_kind} V{wl.target.vocab}",
-                   "draft": f"L{wl.draft.n_layers} d{wl.draft.d_model} F{wl.draft.d_ffn}",
+        "config": {"workload": f"{args.workload}-shape speculative rounds: target "
+                               f"L{wl.target.n_layers} d{wl.target.d_model} F{wl.target.d_ffn} "
+                               f"{wl.target.ffn_kind} V{wl.target.vocab}, draft "
+                               f"L{wl.draft.n_layers} d{wl.draft.d_model} F{wl.draft.d_ffn}",
                    "batch": B, "K": K, "context": wl.ctx, "temperature": wl.temperature,
                    "top_p": wl.top_p, "parallelism": "1 GPU"},
         "verify_ms_median": v_med,
