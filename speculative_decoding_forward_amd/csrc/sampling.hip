@@ -124,22 +124,25 @@ struct RadixResult {
 
 // Largest key t such that the total weight of the participating elements with key
 // >= t reaches `target` (> 0).  kf(x, key) says whether element x takes part and gives
-// its key; wf(x) its integer weight (evaluated only for elements a pass counts).  Three passes over 11-, 11- and 10-bit digits
-// (high to low), each an LDS histogram of the elements whose key matches the digits
-// chosen so far, a block-wide suffix scan over the 2048 bins, and the unique bin
-// where the running weight crosses the target.
-template <int VPT, typename KF, typename WF>
+// its key, whose bits from KB up are zero; wf(x) its integer weight (evaluated only for
+// elements a pass counts).  Three passes over digits of 11, 11 and KB - 22 bits (high to
+// low), each an LDS histogram of the elements whose key matches the digits chosen so far,
+// a block-wide suffix scan over the 2048 bins, and the unique bin where the running
+// weight crosses the target.  Keys with fewer significant bits (KB < 32) spread the
+// first pass over all of its bins, which divides the LDS atomics that collide on a bin.
+template <int VPT, int KB, typename KF, typename WF>
 __device__ __forceinline__ RadixResult radix_select(const float (&v)[VPT], KF kf, WF wf,
                                                     unsigned long long target, VocabLDS& sh) {
+  static_assert(KB > 22 && KB <= 32, "key bits");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t prefix = 0;
   unsigned long long above = 0, kept = 0;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
-    // digit bits [shift, hs); bits [hs, 32) were fixed by the earlier passes
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int hs = pass == 0 ? 31 : (pass == 1 ? 21 : 10);
-    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    // digit bits [shift, hs); bits [hs, KB) were fixed by the earlier passes
+    const int shift = pass == 0 ? KB - 11 : (pass == 1 ? KB - 22 : 0);
+    const int hs = pass == 0 ? KB : (pass == 1 ? KB - 11 : KB - 22);
+    const uint32_t dmask = pass == 2 ? (1u << (KB - 22)) - 1u : 2047u;
     sh.hist[2 * tid] = 0ull;
     sh.hist[2 * tid + 1] = 0ull;
     if (tid == 0) sh.bcast_i[0] = -1;
@@ -256,7 +259,7 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
   // top-k on the logit (the order of l/T is the order of l for T > 0); dropped
   // elements become -inf.  The maximum is always kept.
   if (kn.top_k > 0 && kn.top_k < V) {
-    const RadixResult r = radix_select<VPT>(
+    const RadixResult r = radix_select<VPT, 32>(
         v,
         [](float x, uint32_t& k) {
           k = okey(x);
@@ -290,10 +293,11 @@ __device__ __forceinline__ bool process_row(float (&v)[VPT], int V, const Sampli
     const double ws = invS * 4503599627370496.0;  // 2^52 / S
     const unsigned long long target =
         (unsigned long long)((double)kn.top_p * 4503599627370496.0);
-    const RadixResult r = radix_select<VPT>(
+    const RadixResult r = radix_select<VPT, 30>(
         v,
         [](float e, uint32_t& k) {
-          k = __float_as_uint(e);  // e >= 0: the bit pattern is order-preserving
+          // 0 <= e <= 1: the bit pattern is order-preserving, with bits 30 and 31 zero
+          k = __float_as_uint(e);
           return e > 0.f;
         },
         [=](float e) {
