@@ -12,7 +12,8 @@
 //      V[32k + key(l/16, e)][16u + l%16] for e = 0..7 with key(g, e) = 4g + e (e < 4)
 //      or 16 + 4g + e - 4 -- the B operand of O = P V, in the key order in which the
 //      S^T fragments leave the first product (so P never moves between lanes).
-// Every wave load is therefore 1 KB contiguous.
+// Every wave load is therefore 1 KB contiguous.  From two rows per launch up, K and V are
+// read with non-temporal loads (the launcher's measurements).
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
 // (b, h) and one group of up to 16 queries.  The split count (the grid) is fixed per
@@ -55,11 +56,19 @@ template <int HD> constexpr int attn_ring() { return HD == 128 ? SPEC_ATTN_RING 
 constexpr int AQ = 16;   // queries per group
 constexpr int AKB = 32;  // keys per block
 
+// One 16-byte fragment; STREAM: a non-temporal load (streaming cache policy).
+template <bool STREAM>
 __device__ __forceinline__ bf16x8 ldfrag(const u16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  if constexpr (STREAM) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  } else {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
 }
 
-template <int HD, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
+template <int HD, bool KVNT, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
 __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     const u16* __restrict__ q, int M, int H, const u16* __restrict__ kc,
     const u16* __restrict__ vc, size_t row_stride, size_t head_stride,
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   const u16* qrow = q + (size_t)(b * M + (qok ? jq : 0)) * d + h * HD + 8 * g;
   bf16x8 qf[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = ldfrag(qrow + 32 * s);
+  for (int s = 0; s < NS; ++s) qf[s] = ldfrag<false>(qrow + 32 * s);
   const int qpos = p0 + jq;  // the query's cache position
 
   // Ring of RING blocks.  Block i of this wave is split*bps + wv + AW*i (i < nmine); a
@@ -119,9 +128,9 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        kf[slot][kt][s] = ldfrag(kh + ((size_t)(2 * blk + kt) * NS + s) * 512 + 8 * lane);
+        kf[slot][kt][s] = ldfrag<KVNT>(kh + ((size_t)(2 * blk + kt) * NS + s) * 512 + 8 * lane);
 #pragma unroll
-    for (int u = 0; u < NT; ++u) vf[slot][u] = ldfrag(vh + ((size_t)blk * NT + u) * 512 + 8 * lane);
+    for (int u = 0; u < NT; ++u) vf[slot][u] = ldfrag<KVNT>(vh + ((size_t)blk * NT + u) * 512 + 8 * lane);
   };
   float m = -INFINITY, l = 0.f;  // running max / sum of query nl (replicated over g)
   floatx4 o[NT];                 // O[query 4g + e][dim 16u + nl]
@@ -377,16 +386,25 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
                                  hipEvent_t e0, hipEvent_t e1) {
   const int nsplit = attn_nsplit(B, H, M, max_len);
   const dim3 grid(nsplit, H, B * attn_groups(M));
-  if (hd == 128)
-    hipExtLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(attn_waves<128>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
-                          vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          out);
-  else if (hd == 64)
-    hipExtLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(attn_waves<64>() * 64), 0, s, e0, e1, 0, q, M, H, kc,
-                          vc, row_stride, head_stride, pos0, ntok_eff, part, counters, nsplit,
-                          out);
-  else
+  // K/V streamed with non-temporal loads from two rows up: measured per launch at the 7B
+  // shape and 2048 positions, 8 rows of 6 queries 50.7 -> 45.7 us, 4 rows 29.8 -> 28.2,
+  // 16 rows of one query 49.3 -> 44.5; at one row they were slower (one query 10.9 ->
+  // 12.5 us), so a single row keeps the default policy.
+  const bool nt = B >= 2;
+#define SPEC_ATTN_LAUNCH(HD_, NT_)                                                           \
+  hipExtLaunchKernelGGL(k_attn_bf16<HD_, NT_>, grid, dim3(attn_waves<HD_>() * 64), 0, s, e0, \
+                        e1, 0, q, M, H, kc, vc, row_stride, head_stride, pos0, ntok_eff, part, \
+                        counters, nsplit, out)
+  if (hd == 128) {
+    if (nt) SPEC_ATTN_LAUNCH(128, true);
+    else SPEC_ATTN_LAUNCH(128, false);
+  } else if (hd == 64) {
+    if (nt) SPEC_ATTN_LAUNCH(64, true);
+    else SPEC_ATTN_LAUNCH(64, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef SPEC_ATTN_LAUNCH
   return hipGetLastError();
 }
 
