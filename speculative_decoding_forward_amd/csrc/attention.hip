@@ -12,8 +12,8 @@
 //      V[32k + key(l/16, e)][16u + l%16] for e = 0..7 with key(g, e) = 4g + e (e < 4)
 //      or 16 + 4g + e - 4 -- the B operand of O = P V, in the key order in which the
 //      S^T fragments leave the first product (so P never moves between lanes).
-// Every wave load is therefore 1 KB contiguous.  From two rows per launch up, K and V are
-// read with non-temporal loads (the launcher's measurements).
+// Every wave load is therefore 1 KB contiguous.  K and V are read with non-temporal loads
+// except by launches of one row with one query (the launcher's measurements).
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
 // (b, h) and one group of up to 16 queries.  The split count (the grid) is fixed per
@@ -386,11 +386,13 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
                                  hipEvent_t e0, hipEvent_t e1) {
   const int nsplit = attn_nsplit(B, H, M, max_len);
   const dim3 grid(nsplit, H, B * attn_groups(M));
-  // K/V streamed with non-temporal loads from two rows up: measured per launch at the 7B
-  // shape and 2048 positions, 8 rows of 6 queries 50.7 -> 45.7 us, 4 rows 29.8 -> 28.2,
-  // 16 rows of one query 49.3 -> 44.5; at one row they were slower (one query 10.9 ->
-  // 12.5 us), so a single row keeps the default policy.
-  const bool nt = B >= 2;
+  // K/V streamed with non-temporal loads unless the launch is one row of one query:
+  // measured per launch at the 7B shape and 2048 positions, 8 rows of 6 queries 50.7 ->
+  // 45.7 us, 4 rows 29.8 -> 28.2, 16 rows of one query 49.3 -> 44.5; one row of 6 queries
+  // (the verify pass) 2.833 -> 2.805 ms per pass in replayed rounds, the cached weights and
+  // draft K/V no longer displaced.  One row of one query (a draft step) was slower with
+  // them (10.9 -> 12.5 us per launch): its K/V is re-read every draft step and stays cached.
+  const bool nt = B >= 2 || M >= 2;
 #define SPEC_ATTN_LAUNCH(HD_, NT_)                                                           \
   hipExtLaunchKernelGGL(k_attn_bf16<HD_, NT_>, grid, dim3(attn_waves<HD_>() * 64), 0, s, e0, \
                         e1, 0, q, M, H, kc, vc, row_stride, head_stride, pos0, ntok_eff, part, \
