@@ -337,7 +337,7 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
       SPEC_LAUNCH(launch_attention_bf16((const uint16_t*)w.q, kl, vl, kv->row_stride,
                                         kv->head_stride, B, M, H, hd, w.pos0, w.ntok_eff,
                                         w.part, attn_counters, kv->max_len,
-                                        (uint16_t*)w.att, s, ev.e0, ev.e1));
+                                        (uint16_t*)w.att, l, c.n_layers, s, ev.e0, ev.e1));
     }
     SPEC_TRACE_ACT(attn_out, l, w.att, d);
     {

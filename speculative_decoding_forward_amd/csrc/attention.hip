@@ -13,7 +13,8 @@
 //      or 16 + 4g + e - 4 -- the B operand of O = P V, in the key order in which the
 //      S^T fragments leave the first product (so P never moves between lanes).
 // Every wave load is therefore 1 KB contiguous.  K and V are read with non-temporal loads
-// except by launches of one row with one query (the launcher's measurements).
+// except for the later layers of a model whose K/V fits the memory-side cache
+// (kAttnCacheBudget).
 //
 // Split-KV: workgroup (split, h, b*NG + qg) owns `bps` consecutive 32-key blocks of
 // (b, h) and one group of up to 16 queries.  The split count (the grid) is fixed per
@@ -35,6 +36,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "act_layout.h"
 #include "common.h"
@@ -56,25 +58,29 @@ template <int HD> constexpr int attn_ring() { return HD == 128 ? SPEC_ATTN_RING 
 constexpr int AQ = 16;   // queries per group
 constexpr int AKB = 32;  // keys per block
 
-// One 16-byte fragment; STREAM: a non-temporal load (streaming cache policy).
-template <bool STREAM>
 __device__ __forceinline__ bf16x8 ldfrag(const u16* p) {
-  if constexpr (STREAM) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(bf16x8,
-                              __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
-  } else {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-  }
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-template <int HD, bool KVNT, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
+// One 16-byte K/V fragment at byte offset `off` of a head region, with the cache policy an
+// immediate of the instruction (AUX 2: non-temporal), so that the two policies of the
+// kernel's branch stay distinct instructions.
+template <int AUX>
+__device__ __forceinline__ bf16x8 ldkv(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+
+// K/V bytes of all layers of a model that the memory-side cache (256 MB on MI355X) is left
+// to hold across forwards: the cache policy of the K/V loads below.
+constexpr size_t kAttnCacheBudget = (size_t)240 << 20;
+
+template <int HD, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
 __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     const u16* __restrict__ q, int M, int H, const u16* __restrict__ kc,
     const u16* __restrict__ vc, size_t row_stride, size_t head_stride,
     const int32_t* __restrict__ pos0, const int32_t* __restrict__ ntok_eff,
     float* __restrict__ part, unsigned* __restrict__ counters, int nsplit,
-    u16* __restrict__ out) {
+    u16* __restrict__ out, int layer, int n_layers) {
   constexpr int NS = HD / 32;  // K slices (MFMAs per 16-key tile)
   constexpr int NT = HD / 16;  // dim tiles of O
   __shared__ float wm[AW][AQ], wl[AW][AQ];
@@ -103,6 +109,15 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
     return;
   }
   if (split >= n_active) return;  // uniform over the workgroup
+  // Cache policy of the K/V loads (a hint: results do not depend on it).  A model whose K/V
+  // at this length fits about twice the budget (a draft, a small model) keeps its later
+  // layers in the memory-side cache, where the next forward finds them, and streams its
+  // first layers with non-temporal loads: a K/V stream larger than the cache, read in the
+  // same order every forward, would otherwise evict itself before reuse.  Larger ones (a
+  // 7B or 70B target, any batch of drafts) stream every layer.
+  const size_t layer_bytes = (size_t)(gridDim.z / NG) * 4u * (size_t)H * (size_t)len_end * HD;
+  const bool stream = (size_t)n_layers * layer_bytes > 2 * kAttnCacheBudget ||
+                      layer < n_layers - (int)(kAttnCacheBudget / layer_bytes);
   const u16* kh = kc + (size_t)b * row_stride + (size_t)h * head_stride;
   const u16* vh = vc + (size_t)b * row_stride + (size_t)h * head_stride;
   const float scale = 1.0f / sqrtf((float)HD);
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   const u16* qrow = q + (size_t)(b * M + (qok ? jq : 0)) * d + h * HD + 8 * g;
   bf16x8 qf[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = ldfrag<false>(qrow + 32 * s);
+  for (int s = 0; s < NS; ++s) qf[s] = ldfrag(qrow + 32 * s);
   const int qpos = p0 + jq;  // the query's cache position
 
   // Ring of RING blocks.  Block i of this wave is split*bps + wv + AW*i (i < nmine); a
@@ -122,15 +137,25 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   bf16x8 kf[RING][2][NS];
   bf16x8 vf[RING][NT];
   const int blk0 = split * bps + wv;
-  auto load = [&](int slot, int i) {
-    const int blk = min(blk0 + AW * min(i, max(nmine - 1, 0)), nblk - 1);
+  // buffer resources over this (row, head)'s K and V regions (head_stride elements each)
+  const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(kh, head_stride * 2);
+  const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(vh, head_stride * 2);
+  auto load_policy = [&](auto aux, int slot, int blk) {
+    constexpr int A = decltype(aux)::value;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        kf[slot][kt][s] = ldfrag<KVNT>(kh + ((size_t)(2 * blk + kt) * NS + s) * 512 + 8 * lane);
+        kf[slot][kt][s] =
+            ldkv<A>(rk, (uint32_t)((((2 * blk + kt) * NS + s) * 512 + 8 * lane) * 2));
 #pragma unroll
-    for (int u = 0; u < NT; ++u) vf[slot][u] = ldfrag<KVNT>(vh + ((size_t)blk * NT + u) * 512 + 8 * lane);
+    for (int u = 0; u < NT; ++u)
+      vf[slot][u] = ldkv<A>(rv, (uint32_t)(((blk * NT + u) * 512 + 8 * lane) * 2));
+  };
+  auto load = [&](int slot, int i) {
+    const int blk = min(blk0 + AW * min(i, max(nmine - 1, 0)), nblk - 1);
+    if (stream) load_policy(std::integral_constant<int, 2>{}, slot, blk);
+    else load_policy(std::integral_constant<int, 0>{}, slot, blk);
   };
   float m = -INFINITY, l = 0.f;  // running max / sum of query nl (replicated over g)
   floatx4 o[NT];                 // O[query 4g + e][dim 16u + nl]
@@ -382,30 +407,26 @@ int attn_groups(int M) { return cdiv(M, AQ); }
 hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, size_t row_stride,
                                  size_t head_stride, int B, int M, int H, int hd,
                                  const int32_t* pos0, const int32_t* ntok_eff, float* part,
-                                 unsigned* counters, int max_len, u16* out, hipStream_t s,
-                                 hipEvent_t e0, hipEvent_t e1) {
+                                 unsigned* counters, int max_len, u16* out, int layer,
+                                 int n_layers, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nsplit = attn_nsplit(B, H, M, max_len);
   const dim3 grid(nsplit, H, B * attn_groups(M));
-  // K/V streamed with non-temporal loads unless the launch is one row of one query:
-  // measured per launch at the 7B shape and 2048 positions, 8 rows of 6 queries 50.7 ->
-  // 45.7 us, 4 rows 29.8 -> 28.2, 16 rows of one query 49.3 -> 44.5; one row of 6 queries
-  // (the verify pass) 2.833 -> 2.805 ms per pass in replayed rounds, the cached weights and
-  // draft K/V no longer displaced.  One row of one query (a draft step) was slower with
-  // them (10.9 -> 12.5 us per launch): its K/V is re-read every draft step and stays cached.
-  const bool nt = B >= 2 || M >= 2;
-#define SPEC_ATTN_LAUNCH(HD_, NT_)                                                           \
-  hipExtLaunchKernelGGL(k_attn_bf16<HD_, NT_>, grid, dim3(attn_waves<HD_>() * 64), 0, s, e0, \
-                        e1, 0, q, M, H, kc, vc, row_stride, head_stride, pos0, ntok_eff, part, \
-                        counters, nsplit, out)
-  if (hd == 128) {
-    if (nt) SPEC_ATTN_LAUNCH(128, true);
-    else SPEC_ATTN_LAUNCH(128, false);
-  } else if (hd == 64) {
-    if (nt) SPEC_ATTN_LAUNCH(64, true);
-    else SPEC_ATTN_LAUNCH(64, false);
-  } else {
+  // The kernel picks the K/V cache policy per layer (kAttnCacheBudget).  Measured per launch
+  // at the 7B shape and 2048 positions, non-temporal against ordinary loads: 8 rows of 6
+  // queries 50.7 -> 45.7 us, 4 rows 29.8 -> 28.2, 16 rows of one query 49.3 -> 44.5, and the
+  // one-row verify pass 2.833 -> 2.805 ms in replayed rounds; the one-row draft (about
+  // 270 MB of K/V over 16 layers) 10.9 -> 12.5 us with every layer streamed, 10.6 -> 9.9 us
+  // on average with only its first two layers streamed.
+#define SPEC_ATTN_LAUNCH(HD_)                                                                 \
+  hipExtLaunchKernelGGL(k_attn_bf16<HD_>, grid, dim3(attn_waves<HD_>() * 64), 0, s, e0, e1, 0, \
+                        q, M, H, kc, vc, row_stride, head_stride, pos0, ntok_eff, part,        \
+                        counters, nsplit, out, layer, n_layers)
+  if (hd == 128)
+    SPEC_ATTN_LAUNCH(128);
+  else if (hd == 64)
+    SPEC_ATTN_LAUNCH(64);
+  else
     return hipErrorInvalidValue;
-  }
 #undef SPEC_ATTN_LAUNCH
   return hipGetLastError();
 }

@@ -60,7 +60,8 @@ hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const ui
                                  size_t row_stride, size_t head_stride, int B, int M, int H,
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,
                                  float* part, unsigned* counters, int max_len, uint16_t* out,
-                                 hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                                 int layer, int n_layers, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1);
 constexpr int kAttnMaxCUs = 1024;                     // bound on the CUs a split grid uses
 // completion counters of the split attention sit 128 bytes apart: the atomics of
 // different (row, head, group) units then do not queue on one cache line
