@@ -71,8 +71,9 @@ __device__ __forceinline__ bf16x8 ldkv(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // K/V bytes of all layers of a model that the memory-side cache (256 MB on MI355X) is left
-// to hold across forwards: the cache policy of the K/V loads below.
-constexpr size_t kAttnCacheBudget = (size_t)240 << 20;
+// to hold across forwards: the cache policy of the K/V loads below.  Whole 7B-shape rounds
+// took 6.27-6.28 ms with 200, 224 or 240 MB and 6.30 ms with 256 MB.
+constexpr size_t kAttnCacheBudget = (size_t)224 << 20;
 
 template <int HD, int AW = attn_waves<HD>(), int RING = attn_ring<HD>()>
 __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
