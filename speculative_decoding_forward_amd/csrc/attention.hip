@@ -62,6 +62,13 @@ __device__ __forceinline__ bf16x8 ldfrag(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+// Buffer resource over `bytes` bytes of a K or V head region (offsets past it read zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const u16* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(base), 0,
+                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                           0x00020000);
+}
+
 // One 16-byte K/V fragment at byte offset `off` of a head region, with the cache policy an
 // immediate of the instruction (AUX 2: non-temporal), so that the two policies of the
 // kernel's branch stay distinct instructions.
@@ -139,8 +146,8 @@ __global__ __launch_bounds__(AW * 64) void k_attn_bf16(
   bf16x8 vf[RING][NT];
   const int blk0 = split * bps + wv;
   // buffer resources over this (row, head)'s K and V regions (head_stride elements each)
-  const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(kh, head_stride * 2);
-  const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(vh, head_stride * 2);
+  const __amdgpu_buffer_rsrc_t rk = kv_rsrc(kh, head_stride * 2);
+  const __amdgpu_buffer_rsrc_t rv = kv_rsrc(vh, head_stride * 2);
   auto load_policy = [&](auto aux, int slot, int blk) {
     constexpr int A = decltype(aux)::value;
 #pragma unroll
@@ -416,8 +423,9 @@ hipError_t launch_attention_bf16(const u16* q, const u16* kc, const u16* vc, siz
   // at the 7B shape and 2048 positions, non-temporal against ordinary loads: 8 rows of 6
   // queries 50.7 -> 45.7 us, 4 rows 29.8 -> 28.2, 16 rows of one query 49.3 -> 44.5, and the
   // one-row verify pass 2.833 -> 2.805 ms in replayed rounds; the one-row draft (about
-  // 270 MB of K/V over 16 layers) 10.9 -> 12.5 us with every layer streamed, 10.6 -> 9.9 us
-  // on average with only its first two layers streamed.
+  // 270 MB of K/V over 16 layers) 10.9 -> 12.5 us with every layer streamed, and 10.8 ->
+  // 10.3 us on average with only the layers past the budget streamed (6.39 -> 6.29 ms per
+  // 7B-shape round).
 #define SPEC_ATTN_LAUNCH(HD_)                                                                 \
   hipExtLaunchKernelGGL(k_attn_bf16<HD_>, grid, dim3(attn_waves<HD_>() * 64), 0, s, e0, e1, 0, \
                         q, M, H, kc, vc, row_stride, head_stride, pos0, ntok_eff, part,        \
