@@ -286,14 +286,14 @@ spec_status forward_f32(const spec_model* m, spec_kv* kv, int B, int M, float* l
 //   squares for the next layer's QKV; after the last layer x * g_f in fp32) ->
 //   after the layers: normalise pass (bf16(RMSNorm(x) * g_f)) -> LM head GEMM.
 spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* logits,
-                         const FwdWS& w, hipStream_t s, const Trace* trace) {
+                         const FwdWS& w, hipStream_t s, const Trace* trace, const PrepArgs& pa) {
   const spec_model_cfg& c = m->cfg;
   const int R = B * M, d = c.d_model, F = c.d_ffn, V = c.vocab, H = c.n_heads,
             hd = c.head_dim;
   const size_t e = elt_bytes(c);
   unsigned* attn_counters = w.counters;
-  SPEC_LAUNCH(launch_embed_norm(m->embed, w.tok_eff, R, d, m->layers[0].norm1, w.x, w.h, w.ss,
-                                kv->rope, w.pos0, M, hd, kv->max_len, w.rope_rows, s));
+  SPEC_LAUNCH(launch_embed_norm(m->embed, pa, R, d, m->layers[0].norm1, w.x, w.h, w.ss,
+                                kv->rope, M, hd, kv->max_len, w.rope_rows, s));
   SPEC_TRACE(0);
   GemmArgs base{};
   base.R = R;
@@ -396,7 +396,8 @@ spec_status forward_bf16(const spec_model* m, spec_kv* kv, int B, int M, float* 
     SPEC_TRACE(2 * l + 2);
   }
   // the LM head's input bf16(RMSNorm(x) * g_f), rounded once after the row factor
-  SPEC_LAUNCH(launch_norm_pack(w.xg, w.ss, R, d, c.norm_eps, (uint16_t*)w.h, s));
+  SPEC_LAUNCH(launch_norm_pack(w.xg, w.ss, R, d, c.norm_eps, (uint16_t*)w.h, kv->len,
+                               w.ntok_eff, M, s));
   GemmArgs g = base;
   g.mode = EPI_STORE;
   g.A = (const uint16_t*)w.h;
@@ -419,10 +420,17 @@ spec_status forward(const spec_model* m, spec_kv* kv, const int32_t* tokens,
                     const int32_t* n_tok, int B, int M, float* logits, int32_t* row_status,
                     int record_base, const FwdWS& w, hipStream_t s,
                     const DraftSrc* ds = nullptr, const Trace* trace = nullptr) {
+  if (m->cfg.dtype == SPEC_DT_BF16) {
+    // the row bookkeeping runs inside the embedding kernel (k_embed_norm)
+    const PrepArgs pa{tokens,    n_tok,      m->cfg.vocab,       kv->len,
+                      kv->base,  record_base, w.pos0,            w.ntok_eff,
+                      w.tok_eff, row_status, w.counters,         w.n_counters,
+                      ds ? *ds : DraftSrc{}, ds ? 1 : 0};
+    return forward_bf16(m, kv, B, M, logits, w, s, trace, pa);
+  }
   SPEC_LAUNCH(launch_prep(tokens, n_tok, B, M, m->cfg.vocab, kv->len, kv->base, record_base,
                           kv->max_len, w.pos0, w.ntok_eff, w.tok_eff, row_status, w.counters,
                           w.n_counters, ds, s));
-  if (m->cfg.dtype == SPEC_DT_BF16) return forward_bf16(m, kv, B, M, logits, w, s, trace);
   return forward_f32(m, kv, B, M, logits, w, s, trace);
 }
 

@@ -61,9 +61,12 @@ constexpr int kSkCounterStride = 32;  // 128 bytes between completion counters
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // h = bf16(xg * s_r) in the packed bf16 order for R rows of width K (xg in act32_index
-// order, s_r = 1 / sqrt(sum of the partial sums ss [R][K/16] / K + eps)).
+// order, s_r = 1 / sqrt(sum of the partial sums ss [R][K/16] / K + eps)).  With len, the
+// pass also ends the forward's row bookkeeping: len[b] += ntok_eff[b] for each sequence b
+// of M rows.
 hipError_t launch_norm_pack(const float* xg, const float* ss, int R, int K, float eps,
-                            uint16_t* h, hipStream_t s);
+                            uint16_t* h, int32_t* len, const int32_t* ntok_eff, int M,
+                            hipStream_t s);
 enum { PACK_PLAIN = 0, PACK_QKV = 1, PACK_PAIR_LO = 2, PACK_PAIR_HI = 3 };
 hipError_t launch_pack_bf16(const uint16_t* src, int K, int mode, int d, int hd, int ntiles,
                             uint16_t* dst, hipStream_t s);

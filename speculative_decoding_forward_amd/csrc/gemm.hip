@@ -1023,10 +1023,14 @@ __global__ __launch_bounds__(GT) void k_gemm_sk(GemmArgs g) {
 // then every thread rounds 8-column groups into the packed bf16 order.
 __global__ __launch_bounds__(256) void k_norm_pack(const float* __restrict__ xg,
                                                    const float* __restrict__ ss, int K, float eps,
-                                                   u16* __restrict__ h) {
+                                                   u16* __restrict__ h, int32_t* __restrict__ len,
+                                                   const int32_t* __restrict__ ntok_eff, int M) {
   __shared__ float ssl[SS_NP_MAX];
   __shared__ double rs;
   const int r = blockIdx.x, np = K >> 4;
+  // the length update of the forward's row bookkeeping: every earlier kernel of the forward
+  // has read the old length (the embedding pass) or the start positions derived from it
+  if (len && threadIdx.x == 0 && r % M == 0) len[r / M] += ntok_eff[r / M];
   for (int i = threadIdx.x; i < np; i += 256) ssl[i] = ss[(size_t)r * np + i];
   __syncthreads();
   if (threadIdx.x < 64) row_factors(ssl, 1, np, K, eps, threadIdx.x, &rs);
@@ -1047,9 +1051,9 @@ __global__ __launch_bounds__(256) void k_norm_pack(const float* __restrict__ xg,
 }
 
 hipError_t launch_norm_pack(const float* xg, const float* ss, int R, int K, float eps, u16* h,
-                            hipStream_t s) {
-  if (R < 1 || K % 128 || K / 16 > SS_NP_MAX) return hipErrorInvalidValue;
-  k_norm_pack<<<R, 256, 0, s>>>(xg, ss, K, eps, h);
+                            int32_t* len, const int32_t* ntok_eff, int M, hipStream_t s) {
+  if (R < 1 || K % 128 || K / 16 > SS_NP_MAX || M < 1 || R % M) return hipErrorInvalidValue;
+  k_norm_pack<<<R, 256, 0, s>>>(xg, ss, K, eps, h, len, ntok_eff, M);
   return hipGetLastError();
 }
 

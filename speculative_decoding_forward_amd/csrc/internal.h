@@ -52,10 +52,7 @@ struct SamplingKnobs {
 // kernel launchers (defined in the .hip files)
 namespace specdec {
 
-hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float* x, void* h, float* ss, const double* rope,
-                             const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
-                             hipStream_t s);
+
 hipError_t launch_attention_bf16(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                                  size_t row_stride, size_t head_stride, int B, int M, int H,
                                  int hd, const int32_t* pos0, const int32_t* ntok_eff,
@@ -85,6 +82,26 @@ struct DraftSrc {
   int K, step;
   int32_t* n_tok_out;
 };
+// Row bookkeeping of a forward (k_prep; for bf16 models folded into k_embed_norm).
+struct PrepArgs {
+  const int32_t* tokens;
+  const int32_t* n_tok;
+  int V;
+  int32_t* len;
+  int32_t* base;
+  int record_base;
+  int32_t* pos0;
+  int32_t* ntok_eff;
+  int32_t* tok_eff;
+  int32_t* row_status;
+  unsigned* counters;
+  int n_counters;
+  DraftSrc ds;
+  int draft;
+};
+hipError_t launch_embed_norm(const void* embed, const PrepArgs& pa, int R, int d, const float* g,
+                             float* x, void* h, float* ss, const double* rope, int M, int hd,
+                             int max_len, double* rope_rows, hipStream_t s);
 hipError_t launch_prep(const int32_t* tokens, const int32_t* n_tok, int B, int M, int V,
                        int32_t* len, int32_t* base, int record_base, int max_len,
                        int32_t* pos0, int32_t* ntok_eff, int32_t* tok_eff,

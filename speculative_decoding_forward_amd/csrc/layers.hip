@@ -83,23 +83,67 @@ __global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok
 // 1 / sqrt(mean(x^2) + eps); also the row's RoPE factors for all layers.  One block (256
 // threads) per row; a thread takes one 16-column group at a time (two 16-byte loads; d is
 // a multiple of 128).
+//
+// The same kernel does the row bookkeeping of k_prep (bf16 models have no pass of their
+// own for it): every block computes its sequence's token count, start position and
+// overflow flag from the length, which nothing writes during the forward; block j = 0 of a
+// sequence publishes them, each block its own row's token, and the length update itself
+// is left to the LM head's normalise pass (k_norm_pack), after every reader of the old
+// length.
 __global__ __launch_bounds__(256) void k_embed_norm(
-    const u16* __restrict__ E, const int32_t* __restrict__ tok, int d, const float* __restrict__ g,
+    const u16* __restrict__ E, const PrepArgs pa, int d, const float* __restrict__ g,
     float* __restrict__ x, u16* __restrict__ h, float* __restrict__ ss,
-    const double* __restrict__ rope, const int32_t* __restrict__ pos0, int M, int hd, int max_len,
+    const double* __restrict__ rope, int M, int hd, int max_len,
     double* __restrict__ rope_rows) {
-  const int r = blockIdx.x;
+  const int r = blockIdx.x, b = r / M, j = r - b * M;
+  for (int i = r * 256 + threadIdx.x; i < pa.n_counters; i += gridDim.x * 256)
+    pa.counters[i] = 0u;
+  int n;
+  if (pa.draft) {
+    n = pa.ds.step == 0 ? min(max(pa.ds.n_in[b], 0), 2) : 1;
+  } else {
+    n = pa.n_tok ? pa.n_tok[b] : M;
+  }
+  const int n_req = n;
+  n = min(max(n, 0), M);
+  const int L = pa.len[b];
+  int flags = 0;
+  if (L < 0 || L + n > max_len) {
+    flags |= SPEC_ROW_KV_OVERFLOW;
+    n = 0;
+  }
+  const int p0 = max(L, 0);
+  int tok = 0;
+  if (j < n) {
+    tok = !pa.draft ? pa.tokens[(size_t)b * M + j]
+                    : (pa.ds.step == 0 ? pa.ds.in_tok[2 * b + j]
+                                       : pa.ds.x_tilde[b * pa.ds.K + pa.ds.step - 1]);
+    if (tok < 0 || tok >= pa.V) {
+      flags |= SPEC_ROW_BAD_TOKEN;
+      tok = 0;
+    }
+  }
+  if (threadIdx.x == 0) {
+    pa.tok_eff[r] = tok;
+    if (j == 0) {
+      pa.pos0[b] = p0;
+      pa.ntok_eff[b] = n;
+      if (pa.record_base) pa.base[b] = L;
+      if (pa.draft) pa.ds.n_tok_out[b] = n_req;
+    }
+    if (pa.row_status && flags) atomicOr(&pa.row_status[b], flags);
+  }
   {
     // the row's RoPE factors for every layer of this forward: (cos, sin) at the row's
     // absolute position, copied from the cache's table (rows past a sequence's tokens may
     // sit past max_len; their q and k are never used)
     const int half = hd >> 1;
-    const int pos = min(pos0[r / M] + r % M, max_len - 1);
+    const int pos = min(p0 + j, max_len - 1);
     const double2* src = reinterpret_cast<const double2*>(rope) + (size_t)pos * half;
     double2* dst = reinterpret_cast<double2*>(rope_rows) + (size_t)r * half;
     for (int i = threadIdx.x; i < half; i += 256) dst[i] = src[i];
   }
-  const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)tok[r] * d);
+  const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)tok * d);
   float4* xr = reinterpret_cast<float4*>(x + (size_t)r * d);
   const float4* gr = reinterpret_cast<const float4*>(g);
   // h in the packed activation order (act_layout.h): 8 consecutive columns stay contiguous
@@ -332,12 +376,13 @@ hipError_t launch_attention_f32(const float* q, const float* kcache, const float
 }
 
 
-hipError_t launch_embed_norm(const void* embed, const int32_t* tok_eff, int R, int d,
-                             const float* g, float* x, void* h, float* ss, const double* rope,
-                             const int32_t* pos0, int M, int hd, int max_len, double* rope_rows,
-                             hipStream_t s) {
-  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, tok_eff, d, g, x, (u16*)h, ss, rope, pos0, M,
-                                 hd, max_len, rope_rows);
+hipError_t launch_embed_norm(const void* embed, const PrepArgs& pa, int R, int d, const float* g,
+                             float* x, void* h, float* ss, const double* rope, int M, int hd,
+                             int max_len, double* rope_rows, hipStream_t s) {
+  if (pa.draft && (pa.ds.step < 0 || (pa.ds.step == 0 ? M < 2 : M < 1)))
+    return hipErrorInvalidValue;
+  k_embed_norm<<<R, 256, 0, s>>>((const u16*)embed, pa, d, g, x, (u16*)h, ss, rope, M, hd,
+                                 max_len, rope_rows);
   return hipGetLastError();
 }
 
