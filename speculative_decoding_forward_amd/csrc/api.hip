@@ -153,7 +153,7 @@ FwdWS fwd_layout(const spec_model_cfg& c, int B, int M, int max_len, char* base)
   w.logits = (float*)take(R * V * 4);
   w.ss = (float*)take(c.dtype == SPEC_DT_BF16 ? R * (d / 16) * 4 : 0);
   // slot partials of the residual GEMMs at 2-4 row tiles: [d/16 tiles][4 slots][4][1 KB]
-  w.sk_part = (float*)take(c.dtype == SPEC_DT_BF16 ? (d / 16) * 4 * 4 * 1024 : 0);
+  w.sk_part = (float*)take(c.dtype == SPEC_DT_BF16 ? (d / 16) * 4 * 8 * 1024 : 0);
   w.rowscale = (float*)take(c.dtype == SPEC_DT_F32 ? R * 4 : 0);
   w.rope_rows = (double*)take(c.dtype == SPEC_DT_BF16 ? R * c.head_dim * 8 : 0);
   w.total = off;

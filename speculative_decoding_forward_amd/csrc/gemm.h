@@ -50,10 +50,9 @@ struct GemmArgs {
   uint16_t* h_out;
   float* xg_out;
   float* ss_out;
-  // RESID at 2-4 row tiles with one tile per workgroup (k_gemm_sk): fp32 slot partials
-  // [ntiles][4][row tiles][64 lanes][4] and completion counters [ntiles / 4] kSkCounterStride
-  // words apart, zero at launch (the last workgroup of a group resets its counter); NULL:
-  // that kernel is not used
+  // RESID at 2-8 row tiles (k_gemm_sk): fp32 slot partials [ntiles][4][row tiles][64
+  // lanes][4] and completion counters [ntiles / 4] kSkCounterStride words apart, zero at
+  // launch (the last workgroup of a group resets its counter); NULL: that kernel is not used
   float* sk_part;
   unsigned* sk_counters;
 };

@@ -272,11 +272,11 @@ __device__ __forceinline__ void row_factors(const float* ss, int rows, int np, i
   if (qq == 0 && row < rows) rowscale[row] = 1.0 / sqrt(part / K + (double)eps);
 }
 
-template <int MT>
+template <int MT, int NP = GW>
 __device__ __forceinline__ floatx4 sum_partials(const floatx4 (*part)[MT][64], int mt, int lane) {
   floatx4 v = part[0][mt][lane];
 #pragma unroll
-  for (int w = 1; w < GW; ++w) {
+  for (int w = 1; w < NP; ++w) {
     const floatx4 p = part[w][mt][lane];
     v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
   }
@@ -285,11 +285,12 @@ __device__ __forceinline__ floatx4 sum_partials(const floatx4 (*part)[MT][64], i
 
 // Per-tile epilogue, run by the workgroup's epilogue wave.  part[w][mt][lane] holds
 // wave w's MFMA accumulator fragment of row tile mt: lane l has rows 4(l/16)+e
-// (e = 0..3) of local column l%16.  The GW partials are summed in wave order.
+// (e = 0..3) of local column l%16.  The NP partials are summed in wave order (NP = 1: a
+// fragment the caller has already summed in that order).
 // rowinfo[rr] = (absolute position, flags) of row r0 + rr: flag 1 = a real token of its
 // sequence, flag 2 = its K/V may be written (real token and position < max_len).
 // One loop per mode, so each mode's registers are allocated on its own.
-template <int MT>
+template <int MT, int NP = GW>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int r0,
                                                    const floatx4 (*part)[MT][64],
                                                    const int2* rowinfo, const double* rowscale,
@@ -303,7 +304,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
     const float gc = L.gain[nl];
 #pragma unroll 1
     for (int mt = 0; mt < MT; ++mt) {
-      const floatx4 v = sum_partials<MT>(part, mt, lane);
+      const floatx4 v = sum_partials<MT, NP>(part, mt, lane);
       double sq[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -338,7 +339,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
   // normalised products: the row factor first
 #pragma unroll 1
   for (int mt = 0; mt < MT; ++mt) {
-    floatx4 v = sum_partials<MT>(part, mt, lane);
+    floatx4 v = sum_partials<MT, NP>(part, mt, lane);
     if (g.ss_in) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (float)((double)v[e] * rowscale[mt * 16 + 4 * gq + e]);
@@ -882,17 +883,20 @@ __host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode, int np, b
 // last to finish (completion counter, reset by it) sums the slots in order 0..3 and runs
 // the residual epilogue, so every output is bitwise that of k_gemm_bf16.
 constexpr int SK_SLOTS = GW;  // wave slots of the reference summation order
+constexpr int SK_MT_MAX = 8;  // row tiles of the split-by-slot kernel (128 rows)
 
 #ifndef SPEC_SK_DEPTH
 #define SPEC_SK_DEPTH 2  // steps requested ahead of the one being multiplied
 #endif
 template <int MT>
 __global__ __launch_bounds__(GT) void k_gemm_sk(GemmArgs g) {
-  static_assert(MT >= 2 && MT <= 4, "2-4 row tiles");
+  static_assert(MT >= 2 && MT <= SK_MT_MAX, "2-8 row tiles");
   constexpr int P = SPEC_SK_DEPTH;  // steps in flight ahead of the multiplied one
   constexpr int NB = P + 1;         // A buffers (LDS) and W buffers (registers)
   __shared__ uint4 abuf[NB][MT][4][64];               // A fragments of NB steps
-  __shared__ floatx4 part[GW][SK_SLOTS][MT][64];      // merger: [tile of wave][slot][mt][lane]
+  // merger, up to 4 row tiles: [tile of wave][slot][mt][lane]; from 5 on the four slots
+  // are summed in registers and the sums reuse the A ring (the stream has ended)
+  __shared__ floatx4 part[MT <= 4 ? GW : 1][MT <= 4 ? SK_SLOTS : 1][MT <= 4 ? MT : 1][64];
   __shared__ int2 rowinfo[MT * 16];
   __shared__ double rowscale[MT * 16];
   __shared__ int is_last;
@@ -999,20 +1003,46 @@ __global__ __launch_bounds__(GT) void k_gemm_sk(GemmArgs g) {
   const int t = grp * GW + wv;
   const __amdgpu_buffer_rsrc_t rp =
       coherent_rsrc(g.sk_part, (size_t)g.ntiles * SK_SLOTS * MT * 1024);
-#pragma unroll
-  for (int qq = 0; qq < SK_SLOTS; ++qq)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      part[wv][qq][mt][lane] =
-          qq == q ? acc[mt]
-                  : __builtin_amdgcn_raw_buffer_load_b128(
-                        rp, (uint32_t)(((t * SK_SLOTS + qq) * MT + mt) * 1024 + 16 * lane), 0,
-                        kCoherentSc1);
-  wave_lds_sync();
   EpiLds L{};
   L.xres = xres + wv * MT * 16 * 16;
   L.gain = gain + wv * 16;
-  gemm_tile_epilogue<MT>(g, t, 0, part[wv], rowinfo, rowscale, L, lane);
+  if constexpr (MT <= 4) {
+#pragma unroll
+    for (int qq = 0; qq < SK_SLOTS; ++qq)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        part[wv][qq][mt][lane] =
+            qq == q ? acc[mt]
+                    : __builtin_amdgcn_raw_buffer_load_b128(
+                          rp, (uint32_t)(((t * SK_SLOTS + qq) * MT + mt) * 1024 + 16 * lane), 0,
+                          kCoherentSc1);
+    wave_lds_sync();
+    gemm_tile_epilogue<MT>(g, t, 0, part[wv], rowinfo, rowscale, L, lane);
+  } else {
+    // every slot's partial from the stores above (this one's included, bit for bit), all
+    // requested at once, then summed in slot order 0..3 -- the order the epilogue's own
+    // sum of slot partials uses -- into this wave's region of the A ring
+    floatx4 ps[SK_SLOTS][MT];
+#pragma unroll
+    for (int qq = 0; qq < SK_SLOTS; ++qq)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ps[qq][mt] = __builtin_amdgcn_raw_buffer_load_b128(
+            rp, (uint32_t)(((t * SK_SLOTS + qq) * MT + mt) * 1024 + 16 * lane), 0, kCoherentSc1);
+    floatx4(*sums)[MT][64] = reinterpret_cast<floatx4(*)[MT][64]>(&abuf[0][0][0][0]);
+    static_assert(sizeof(abuf) >= sizeof(floatx4) * GW * MT * 64, "sums fit the A ring");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      floatx4 v = ps[0][mt];
+#pragma unroll
+      for (int qq = 1; qq < SK_SLOTS; ++qq) {
+        v[0] += ps[qq][mt][0]; v[1] += ps[qq][mt][1]; v[2] += ps[qq][mt][2]; v[3] += ps[qq][mt][3];
+      }
+      sums[wv][mt][lane] = v;
+    }
+    wave_lds_sync();
+    gemm_tile_epilogue<MT, 1>(g, t, 0, &sums[wv], rowinfo, rowscale, L, lane);
+  }
 }
 
 // ------------------------------------------------------------------ normalise pass --
@@ -1160,17 +1190,25 @@ hipError_t launch_gemm_bf16(const GemmArgs& g0, hipStream_t s, hipEvent_t e0, hi
   if (g.ss_in && (g.ss_np > SS_NP_MAX || g.ss_np % 8)) return hipErrorInvalidValue;
   if (g.mode == EPI_QKV_ROPE && g.hd > 2 * ROPE_HALF_MAX) return hipErrorInvalidValue;
   const int mt = std::min(tiles, 4);
-  if (g.mode == EPI_RESID && mt >= 2 && rowblocks == 1 && g.ntiles % SK_SLOTS == 0 &&
-      g.ntiles <= gmax && g.sk_part && g.sk_counters) {
-    // residual products owning one tile per workgroup: four tiles per workgroup, one wave
-    // slot each, A shared across the tiles
-    const unsigned lds = (unsigned)(GW * (mt * 16 * 16 * 4 + 16 * 4));
-    if (mt == 2)
-      hipExtLaunchKernelGGL(k_gemm_sk<2>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
-    else if (mt == 3)
-      hipExtLaunchKernelGGL(k_gemm_sk<3>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
-    else
-      hipExtLaunchKernelGGL(k_gemm_sk<4>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g);
+  if (g.mode == EPI_RESID && tiles >= 2 && tiles <= SK_MT_MAX && g.ntiles % SK_SLOTS == 0 &&
+      g.ntiles <= device_cus() * SPEC_GEMM_WPC && g.sk_part && g.sk_counters) {
+    // residual products owning one tile per workgroup (2-4 row tiles), and every residual
+    // product of 5-8 row tiles: four tiles per workgroup, one wave slot each, A shared
+    // across the tiles -- up to 128 rows, so the weights stream once (the other kernels
+    // stream them once per 64 rows)
+    const unsigned lds = (unsigned)(GW * (tiles * 16 * 16 * 4 + 16 * 4));
+#define SPEC_SK_LAUNCH(MT_) \
+  hipExtLaunchKernelGGL(k_gemm_sk<MT_>, dim3(g.ntiles), dim3(GT), lds, s, e0, e1, 0, g)
+    switch (tiles) {
+      case 2: SPEC_SK_LAUNCH(2); break;
+      case 3: SPEC_SK_LAUNCH(3); break;
+      case 4: SPEC_SK_LAUNCH(4); break;
+      case 5: SPEC_SK_LAUNCH(5); break;
+      case 6: SPEC_SK_LAUNCH(6); break;
+      case 7: SPEC_SK_LAUNCH(7); break;
+      default: SPEC_SK_LAUNCH(8); break;
+    }
+#undef SPEC_SK_LAUNCH
     return hipGetLastError();
   }
   {

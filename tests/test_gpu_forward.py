@@ -167,15 +167,17 @@ def test_rollback():
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
                                          ("small", 8, 7), ("7b", 8, 7), ("7b", 8, 3),
                                          ("7b", 5, 6), ("70b", 1, 4), ("7b", 16, 4),
-                                         ("small", 12, 7)])
+                                         ("small", 12, 7), ("7b", 16, 7)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
     layers of the target, teacher-forced half by half (tests/helpers_trace.py), with the
     rows' cache lengths staggered by 7 positions.  Rows 6 and 5 take the one-row-tile GEMM
     that forms its normalised input itself; 32, 35 (a ragged last row tile), 48 and 64
     rows the normalise pass and the K-outer GEMM with two to four row tiles where a
-    workgroup owns several column tiles, else the tile-at-a-time one; 80 and 96 rows split
-    into row blocks of at most 64 (64 + 16 and 64 + 32), each on its share of the grid."""
+    workgroup owns several column tiles, else the tile-at-a-time one; 80, 96 and 128 rows
+    split the normalised products into row blocks of at most 64 (64 + 16, 64 + 32, 64 + 64),
+    each on its share of the grid, and run the residual products split by wave slot over
+    all 5, 6 or 8 row tiles at once."""
     wl = synth.WORKLOADS[wl_name]
     shape = dataclasses.replace(wl.target, n_layers=2)
     t = traced_verify(shape, B, K + 1, [wl.ctx - 7 * b for b in range(B)], seed=0)
@@ -224,14 +226,17 @@ def test_draft_steps_match_oracle(B, n_in):
 
 
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, None), ("7b", 1, None), ("7b", 8, None),
-                                         ("7b", 8, 3), ("7b", 8, 7), ("small", 8, 5)])
+                                         ("7b", 8, 3), ("7b", 8, 7), ("small", 8, 5),
+                                         ("7b", 16, 4), ("7b", 16, 7)])
 def test_verify_equals_single_token_calls_bitwise(wl_name, B, K):
     """At full size: one call over K+1 positions gives bitwise the logits of K+1
     one-token calls (the premise of the verify pass), and the appended cache entries
     are bitwise equal; repeating the call is bitwise deterministic.  At B = 8 the verify
     rows span 2, 3 and 4 row tiles (32, 48 and 64 rows), where the residual products run
     split by wave slot over four-tile workgroups (8 rows of one-token calls: one row tile,
-    tile at a time); the small model's residual products have 128 tiles (32 groups)."""
+    tile at a time); the small model's residual products have 128 tiles (32 groups).  At
+    B = 16 (80 and 128 rows) the residual products take all 5 or 8 row tiles in one pass
+    and the other products two row blocks (16 rows of one-token calls: one row tile)."""
     wl = synth.WORKLOADS[wl_name]
     K = K or wl.K
     shape = wl.target
