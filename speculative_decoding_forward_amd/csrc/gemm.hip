@@ -41,7 +41,8 @@
 // Kernels by row count: k_gemm_bf16 (one row tile; and several row tiles with one tile
 // group per workgroup), k_gemm_bf16_ko (2-4 row tiles, several tiles per workgroup: A loaded
 // once per step for a chunk of tiles), k_gemm_sk (residual products at 2-4 row tiles that
-// would own one tile per workgroup: four tiles per workgroup, split by wave slot).  All
+// would own one tile per workgroup, and at 5-8 row tiles: four tiles per workgroup, split by
+// wave slot).  All
 // three accumulate every output element over the same steps in the same order, so a verify
 // call equals single-token calls bit for bit.
 //
@@ -872,7 +873,9 @@ __host__ __device__ inline int ko_lds_bytes(int mt, int tpw, int mode, int np, b
 // workgroup would own a single 16-column tile: the tile-at-a-time kernel then reads the
 // whole A operand (all rows, all K) once per tile, 3 KB of A per KB of weights at 48 rows,
 // and that A traffic from L2 -- not the weight stream -- set its time (with A read from a
-// cached zero block instead, wo + down took 0.95 instead of 1.52 ms per 48-row pass).
+// cached zero block instead, wo + down took 0.95 instead of 1.52 ms per 48-row pass).  At
+// 5-8 row tiles (up to 128 rows) it takes every row in one pass where the other kernels
+// stream the weights once per 64 rows (96-row verify GEMMs 6.94 -> 6.35 ms).
 //
 // Here a workgroup owns four tiles (one per streaming wave) and ONE of the four wave
 // slots of k_gemm_bf16: slot q accumulates super-steps q, q + 4, ... of each tile in
