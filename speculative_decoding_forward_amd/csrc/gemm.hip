@@ -295,7 +295,8 @@ template <int MT, int NP = GW>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int r0,
                                                    const floatx4 (*part)[MT][64],
                                                    const int2* rowinfo, const double* rowscale,
-                                                   const EpiLds& L, int lane) {
+                                                   const EpiLds& L, int lane, int mt0 = 0,
+                                                   int mt1 = MT) {
   const int nl = lane & 15, gq = lane >> 4, R = g.R, mode = g.mode;
   const bool is_hi = nl >= 8;
   if (mode == EPI_RESID) {
@@ -304,7 +305,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
     const int col = 16 * t + nl, np = g.N >> 4;
     const float gc = L.gain[nl];
 #pragma unroll 1
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = mt0; mt < mt1; ++mt) {
       const floatx4 v = sum_partials<MT, NP>(part, mt, lane);
       double sq[4];
 #pragma unroll
@@ -339,7 +340,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
   }
   // normalised products: the row factor first
 #pragma unroll 1
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = mt0; mt < mt1; ++mt) {
     floatx4 v = sum_partials<MT, NP>(part, mt, lane);
     if (g.ss_in) {
 #pragma unroll
@@ -846,15 +847,17 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
     }
     if (wv == GW) __builtin_amdgcn_s_barrier();  // the streaming waves' slot barrier
     __syncthreads();  // partials, row factors and the chunk's staged inputs are complete
+    // the chunk's (tile, row tile) epilogues, spread over all five waves
 #pragma unroll 1
-    for (int j = wv; j < TPW; j += GW + 1) {
+    for (int it = wv; it < TPW * MT; it += GW + 1) {
+      const int j = it / MT, mt = it - j * MT;
       const int t = bx + G * (c * TPW + j);
       if (t >= g.ntiles) break;
       EpiLds Lj = L;
       Lj.rope = L.rope + j * MT * 16 * 8;
       Lj.xres = L.xres + j * MT * 16 * 16;
       Lj.gain = L.gain + j * 16;
-      gemm_tile_epilogue<MT>(g, t, r0, part[j], rowinfo, rowscale, Lj, lane);
+      gemm_tile_epilogue<MT>(g, t, r0, part[j], rowinfo, rowscale, Lj, lane, mt, mt + 1);
     }
     __syncthreads();  // the chunk's partials and input slots may be reused
   }
