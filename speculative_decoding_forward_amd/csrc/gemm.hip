@@ -251,6 +251,36 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* 
                                            voff, soff, 0, 0);
 }
 
+// Cross-lane moves inside a row of 16 lanes by DPP (a vector ALU operation of a few
+// cycles) instead of the LDS crossbar of __shfl (ds_bpermute, an LDS round trip).
+// CTRL: 0xB1 lane ^ 1 and 0x4E lane ^ 2 (quad permutes), 0x141 mirror within each half row
+// of 8, 0x140 mirror within the row, 0x128 rotate the row by 8 (lane ^ 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const unsigned hi =
+      (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Sum over the 16 lanes of a row, bitwise the xor butterfly (^1, ^2, ^4, ^8): after the two
+// quad steps every lane of a quad holds the same sum, so pairing each lane with any lane of
+// the other quad of its half row (the half-row mirror), then with any lane of the other
+// half (the row mirror), adds the same two values as ^4 and ^8 do.
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return v;
+}
+
 // Wait for this wave's outstanding global loads, direct-to-LDS ones included.
 __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -268,8 +298,8 @@ __device__ __forceinline__ void row_factors(const float* ss, int rows, int np, i
       part += ((double)src[c] + (double)src[c + 1]) + ((double)src[c + 2] + (double)src[c + 3]);
     for (int c = per & ~3; c < per; ++c) part += (double)src[c];
   }
-  part += __shfl_xor(part, 1, 64);
-  part += __shfl_xor(part, 2, 64);
+  part += dpp_f64<0xB1>(part);  // lane ^ 1
+  part += dpp_f64<0x4E>(part);  // lane ^ 2
   if (qq == 0 && row < rows) rowscale[row] = 1.0 / sqrt(part / K + (double)eps);
 }
 
@@ -325,9 +355,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
       }
       // sum over the 16 columns of the tile (the 16 lanes of this row group), fixed order
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sq[e] += __shfl_xor(sq[e], o, 64);
+      for (int e = 0; e < 4; ++e) sq[e] = row16_sum(sq[e]);
       if (nl == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -353,7 +381,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
       for (int e = 0; e < 4; ++e) {
         const int rr = mt * 16 + 4 * gq + e, r = r0 + rr;
         const float y = v[e];
-        const float yp = __shfl_xor(y, 8);  // the paired column c ^ 8 of the same row
+        const float yp = dpp_f32<0x128>(y);  // the paired column c ^ 8 of the same row
         if (r >= R) continue;
         u16 o;
         if (qt.sec < 2) {
@@ -382,7 +410,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& g, int t, int
       for (int e = 0; e < 4; ++e) {
         const int r = r0 + mt * 16 + 4 * gq + e;
         const float y = v[e];
-        const float yp = __shfl_xor(y, 8);  // the up column paired with gate column nl
+        const float yp = dpp_f32<0x128>(y);  // the up column paired with gate column nl
         if (r < R && !is_hi)
           g.act_out[act_index(r, 8 * t + nl, g.N1)] = f32_to_bf16(y / (1.f + expf(-y)) * yp);
       }
