@@ -734,8 +734,11 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
   for (int c = 0; c < nchunks; ++c) {
     if (wv == GW) {
       if (c == 0) {
-        // requests first: counts and start positions, the first 16 rows' sums of squares,
-        // the chunk's epilogue inputs; then the streaming waves start
+        // counts and start positions, the first 16 rows' sums of squares and the chunk's
+        // epilogue inputs.  Up to three row tiles they are requested beside the streaming
+        // waves' first steps (needed only at the chunk's end; holding the streams back
+        // behind them cost about 1 us per 48-row launch).  At four row tiles the streams
+        // wait for them: the four batches of row sums must be back before the stream ends.
         int ntok[(MT * 16 + 63) / 64], p0v[(MT * 16 + 63) / 64];
 #pragma unroll
         for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
@@ -745,9 +748,11 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
         }
         if (g.ss_in) lds_copy(g.ss_in + (size_t)r0 * np, L.ss, min(16, rows) * np * 4, lane);
         stage_chunk(0);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MT == 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int k = 0; k < (MT * 16 + 63) / 64; ++k) {
           const int rr = lane + 64 * k, r = r0 + rr;
@@ -777,9 +782,11 @@ __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
         wait_vm();
       }
     } else {
-      if (c == 0) {
-        __builtin_amdgcn_s_barrier();  // the epilogue wave's requests go first
-        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MT == 4) {
+        if (c == 0) {
+          __builtin_amdgcn_s_barrier();  // the epilogue wave's requests go first
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       floatx4 acc[TPW][MT];
 #pragma unroll
