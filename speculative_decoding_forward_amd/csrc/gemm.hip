@@ -682,9 +682,9 @@ template <int MT> constexpr int ko_tpw_max() { return MT == 4 ? 5 : 8; }
 
 // WAUX: the cache policy of the weight loads (an immediate of each load).  Non-temporal (2)
 // by default.  A launch with several 64-row blocks takes ordinary loads (0): its row blocks
-// of one column group run side by side on one XCD (the grid's x extent is a multiple of 8)
-// and stream the same tiles in the same order, so the later request finds the line in
-// L2.  With non-temporal loads a 96-row verify's qkv, gate/up and LM head fetched 1.7-2.1x
+// of one column group run side by side on one XCD (the launcher makes the grid's x extent
+// a multiple of 8 where the grid allows) and stream the same tiles in the same order, so
+// the later request finds the line in L2.  With non-temporal loads a 96-row verify's qkv, gate/up and LM head fetched 1.7-2.1x
 // their weight bytes from HBM.
 template <int MT, int TPW, int WAUX = 2>
 __global__ __launch_bounds__(GT) void k_gemm_bf16_ko(GemmArgs g, int per) {
