@@ -62,3 +62,20 @@ def test_speedup_formula_matches_oracle(alpha, K, c):
     assert bench.speedup_formula(alpha, K, c) == pytest.approx(
         theory.walltime_improvement(alpha, K, c), rel=1e-12)
 
+
+
+def test_recorded_traffic_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    """The line's `traffic` comes from the committed counter summary only while the GEMM
+    sources hash to the value recorded with it; otherwise (other sources, no summary) it
+    is None, never a stale figure."""
+    summary = tmp_path / "traffic.md"
+    current = bench.gemm_source_hash()
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(summary))
+    assert bench.recorded_traffic() is None                       # no summary
+    summary.write_text(f"traffic_bytes_per_launch: 123456\nkernel_sources_sha256: {current}\n")
+    assert bench.recorded_traffic() == 123456.0
+    other = "0" * 16 if current != "0" * 16 else "1" * 16
+    summary.write_text(f"traffic_bytes_per_launch: 123456\nkernel_sources_sha256: {other}\n")
+    assert bench.recorded_traffic() is None                       # taken on other sources
+    summary.write_text(f"kernel_sources_sha256: {current}\n")
+    assert bench.recorded_traffic() is None                       # no figure
