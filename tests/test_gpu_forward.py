@@ -167,7 +167,7 @@ def test_rollback():
 @pytest.mark.parametrize("wl_name,B,K", [("small", 1, 4), ("7b", 1, 5), ("7b", 8, 5),
                                          ("small", 8, 7), ("7b", 8, 7), ("7b", 8, 3),
                                          ("7b", 5, 6), ("70b", 1, 4), ("7b", 16, 4),
-                                         ("small", 12, 7), ("7b", 16, 7)])
+                                         ("small", 12, 7), ("7b", 16, 7), ("70b", 16, 4)])
 def test_full_width_two_layers(wl_name, B, K):
     """Full-width layers (d, F, H, V and context of the workload) on the first two
     layers of the target, teacher-forced half by half (tests/helpers_trace.py), with the
@@ -175,8 +175,9 @@ def test_full_width_two_layers(wl_name, B, K):
     that forms its normalised input itself; 32, 35 (a ragged last row tile), 48 and 64
     rows the normalise pass and the K-outer GEMM with two to four row tiles where a
     workgroup owns several column tiles, else the tile-at-a-time one; 80, 96 and 128 rows
-    split the normalised products into row blocks of at most 64 (64 + 16, 64 + 32, 64 + 64),
-    each on its share of the grid, and run the residual products split by wave slot over
+    split the normalised products into row blocks of at most 64 (64 + 16, 64 + 32, 64 + 64)
+    that read the weights with ordinary loads, side by side on one XCD (the 70B shape's 80
+    rows at d = 8192 among them), and run the residual products split by wave slot over
     all 5, 6 or 8 row tiles at once."""
     wl = synth.WORKLOADS[wl_name]
     shape = dataclasses.replace(wl.target, n_layers=2)
