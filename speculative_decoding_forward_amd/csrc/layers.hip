@@ -98,6 +98,12 @@ __global__ __launch_bounds__(256) void k_embed_norm(
   const int r = blockIdx.x, b = r / M, j = r - b * M;
   for (int i = r * 256 + threadIdx.x; i < pa.n_counters; i += gridDim.x * 256)
     pa.counters[i] = 0u;
+  // the row's token is requested together with the counts and length (an in-bounds read
+  // either way; it is used only for a row below the sequence's count), so the embedding
+  // row waits for one round trip, not two
+  const int tok_in = !pa.draft ? pa.tokens[(size_t)b * M + j]
+                               : (pa.ds.step == 0 ? pa.ds.in_tok[2 * b + min(j, 1)]
+                                                  : pa.ds.x_tilde[b * pa.ds.K + pa.ds.step - 1]);
   int n;
   if (pa.draft) {
     n = pa.ds.step == 0 ? min(max(pa.ds.n_in[b], 0), 2) : 1;
@@ -115,9 +121,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(
   const int p0 = max(L, 0);
   int tok = 0;
   if (j < n) {
-    tok = !pa.draft ? pa.tokens[(size_t)b * M + j]
-                    : (pa.ds.step == 0 ? pa.ds.in_tok[2 * b + j]
-                                       : pa.ds.x_tilde[b * pa.ds.K + pa.ds.step - 1]);
+    tok = tok_in;
     if (tok < 0 || tok >= pa.V) {
       flags |= SPEC_ROW_BAD_TOKEN;
       tok = 0;
