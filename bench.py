@@ -36,7 +36,8 @@ GEMM_SOURCES = ["speculative_decoding_forward_amd/csrc/gemm.hip",
                 "speculative_decoding_forward_amd/csrc/common.h",
                 "speculative_decoding_forward_amd/csrc/gemm.h",
                 "speculative_decoding_forward_amd/csrc/kv_layout.h",
-                "speculative_decoding_forward_amd/csrc/act_layout.h"]
+                "speculative_decoding_forward_amd/csrc/act_layout.h",
+                "speculative_decoding_forward_amd/build_lib.py"]  # the compile flags
 
 
 def parse():

@@ -16,8 +16,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecdec.so")
 ARCH = "gfx950"
 
+# Kernel arguments preloaded into SGPRs (up to 16 dwords): a kernel's first instructions
+# then need no scalar loads of its argument block (whole 7B-shape rounds 6.245 -> 6.234 ms).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-Wno-unused-result"]
 
 
